@@ -1,0 +1,173 @@
+/*
+ * fe.h -- C ABI of libfe.so: paged grouped-query attention over a
+ * block-allocated KV cache, hand-written HIP for MI355X (gfx950).
+ *
+ * The operations are the per-layer attention step of the prefill-then-decode
+ * loop that "Make the Engine Talk" (inference-engine book, chapter 1) walks
+ * through in sections 1.2 and 1.3: one pass over the prompt primes the cache,
+ * then one pass per generated token, and grouped-query attention is one of
+ * the forward pass's mechanisms.  The ForgeEngine README
+ * (github.com/marcoharuni/forge-engine), table "What it implements", gives
+ * the cache as a paged block allocator and the kernels as a CUDA paged GQA
+ * kernel plus a restricted prefill lab; its architecture flowchart has the
+ * prefill/decode step both write to and read from the paged cache.
+ *
+ * Shapes and layout (the pages fix none of them; these are this library's):
+ *   D  = head_dim            -- must be 128
+ *   BS = KV block size       -- must be 16 tokens
+ *   Hq query heads, Hkv KV heads, Hq % Hkv == 0, G = Hq / Hkv in 1..8;
+ *   query head h reads KV head h / G (contiguous groups).
+ *   K and V pools: bf16 [num_blocks][Hkv][BS][D] each, so every
+ *     (block, KV head) tile is one contiguous 4 KiB run.
+ *   slot = block * BS + offset_in_block (int32).
+ *   block_tables: int32 [B][max_blocks_per_seq], row b lists sequence b's
+ *     blocks in token order; token t of sequence b lives in block
+ *     block_tables[b][t / BS] at offset t % BS.
+ *   context_lens[b] (int32) counts every token sequence b attends over,
+ *     including the ones appended this step.
+ *   Attention is softmax(scale * q . k_t) v over tokens t < L, accumulated in
+ *   fp32; out is rounded to bf16 (nearest even); lse is the natural-log
+ *   log-sum-exp  log sum_t exp(scale * q . k_t)  in fp32.
+ *
+ * Conventions:
+ *   - Every pointer argument is DEVICE memory owned by the caller, except
+ *     where marked.  The library allocates nothing and keeps no mutable global
+ *     state; calls on different streams touching disjoint buffers are
+ *     independent.
+ *   - Every call is asynchronous on `stream` (0 = the null stream).  One
+ *     stream orders an append before the attention that reads it.
+ *   - Return value: FE_OK (0), or a negative fe_status.  Argument errors are
+ *     detected on the host before anything is enqueued, so outputs are
+ *     untouched on error.  A failed launch returns FE_ERR_HIP.
+ *     fe_last_error() then gives a per-thread message.  No C++ exception
+ *     crosses this boundary.
+ *   - Device-array contents are not checked on the host (that would need a
+ *     synchronisation).  Kernels clamp instead of faulting: block ids are
+ *     clamped into [0, num_blocks), context lengths into
+ *     [0, min(max_context_len, max_blocks_per_seq * BS)], and append slots
+ *     outside [0, num_blocks * BS) are skipped.  Out-of-contract contents
+ *     thus give unspecified results, never an out-of-bounds access.
+ *   - Defined edge cases: a context length of 0 gives out = 0 and
+ *     lse = -inf; block-table entries past ceil(L / BS) and pool slots past
+ *     token L - 1 of a sequence's last block are never used (their contents,
+ *     NaN included, cannot reach the output).
+ */
+#ifndef FE_H_
+#define FE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FE_OK = 0,
+  FE_ERR_NULL = -1,         /* a required pointer is NULL */
+  FE_ERR_INVALID_ARG = -2,  /* negative/zero size, Hq % Hkv != 0, non-finite scale, ... */
+  FE_ERR_UNSUPPORTED = -3,  /* a valid shape this build has no kernel for (D != 128, BS != 16, G > 8) */
+  FE_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than the size query returns */
+  FE_ERR_HIP = -5,          /* the HIP runtime reported an error at launch */
+  FE_ERR_INTERNAL = -6
+} fe_status;
+
+/*
+ * KV append: scatter new K/V rows into their cache slots.
+ *   For every i in [0, T) with s = slot_mapping[i] in [0, num_blocks * BS):
+ *     k_cache[s / BS][g][s % BS][:] = k_new[i][g][:]  for every KV head g,
+ *     and the same for v.  A negative slot is padding and is skipped.
+ *   This is a bit-exact copy; no other byte of the pools changes.
+ *   k_new, v_new   bf16 [T][Hkv][D]
+ *   slot_mapping   int32 [T]; slots must be distinct within one call
+ *   k_cache, v_cache  bf16 [num_blocks][Hkv][BS][D], updated in place
+ *   T == 0 is a valid no-op (pointers may then be NULL).
+ * Source: ForgeEngine README, "What it implements" (paged KV cache) and the
+ * architecture flowchart's write edge from prefill/decode into the cache.
+ */
+int fe_paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_cache,
+                       void* v_cache, int T, int num_blocks, int Hkv, int D, int BS, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fe_paged_gqa_decode needs for these sizes and
+ * this num_partitions (0 = the automatic choice, which depends only on the
+ * arguments here).  Host-only; returns 0 when no workspace is needed
+ * (single partition) and (size_t)-1 for invalid sizes.
+ */
+size_t fe_paged_gqa_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len,
+                                          int num_partitions);
+
+/*
+ * Number of KV partitions fe_paged_gqa_decode uses for these arguments
+ * (num_partitions 0 = automatic).  Host-only; -1 for invalid sizes.
+ */
+int fe_paged_gqa_decode_num_partitions(int B, int Hq, int Hkv, int D, int max_context_len,
+                                       int num_partitions);
+
+/*
+ * Paged GQA decode: one query token per sequence over its block table.
+ *   out           bf16 [B][Hq][D]
+ *   lse           fp32 [B][Hq] natural log, or NULL
+ *   q             bf16 [B][Hq][D]
+ *   k_cache, v_cache  bf16 [num_blocks][Hkv][BS][D]
+ *   block_tables  int32 [B][max_blocks_per_seq]
+ *   context_lens  int32 [B]
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid)
+ *   scale         softmax scale (usually fp32(1/sqrt(D))), must be finite
+ *   num_partitions  split-K factor: the longest context is cut into this
+ *                 many block-aligned ranges of equal size; each is reduced
+ *                 to a normalised fp32 partial and an LSE, and a second
+ *                 kernel merges them by log-sum-exp.  0 = automatic, 1 = one
+ *                 pass with no workspace.
+ *   workspace     device scratch of at least
+ *                 fe_paged_gqa_decode_workspace_size(...) bytes (may be NULL
+ *                 when that size is 0); owned by the caller, contents
+ *                 clobbered.
+ * Source: ForgeEngine README, "What it implements" (CUDA paged GQA kernel);
+ * "Make the Engine Talk" section 1.2 (one pass per generated token) and
+ * section 1.3 (grouped-query attention).
+ */
+int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                        int B, int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len,
+                        float scale, int num_partitions, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * Paged GQA prefill of a causal query chunk against the cached prefix.
+ *   q              bf16 [total_q][Hq][D], sequences packed back to back
+ *   query_start_loc  int32 [B + 1] DEVICE array; sequence b owns packed rows
+ *                  query_start_loc[b] .. query_start_loc[b+1] - 1 (C_b rows)
+ *   context_lens   int32 [B]: prefix + chunk; the chunk's K/V must already
+ *                  be in the cache (fe_paged_kv_append on the same stream)
+ *   Row query_start_loc[b] + i sits at position L_b - C_b + i and attends to
+ *   tokens 0 .. L_b - C_b + i (bottom-right causal alignment).
+ *   out            bf16 [total_q][Hq][D]
+ *   lse            fp32 [total_q][Hq] natural log, or NULL
+ *   max_q_len      host-side upper bound of every C_b (sizes the grid)
+ *   max_context_len  host-side upper bound of context_lens
+ *   QK^T and PV run on the bf16 MFMA units with fp32 accumulation; the
+ *   softmax weights are rounded to bf16 for the PV product.
+ * Source: ForgeEngine README, "What it implements" (restricted prefill lab)
+ * and "Scheduling" (token-budgeted batching, which cuts prompts into
+ * chunks); "Make the Engine Talk" section 1.2 (the prefill pass).
+ */
+int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32_t* query_start_loc,
+                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                               int max_blocks_per_seq, const int32_t* context_lens, int B, int total_q,
+                               int max_q_len, int Hq, int Hkv, int D, int BS, int num_blocks,
+                               int max_context_len, float scale, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* fe_status_string(int status);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char* fe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FE_H_ */

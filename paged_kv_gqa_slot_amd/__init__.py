@@ -1,0 +1,18 @@
+"""Paged grouped-query attention over a block-allocated KV cache, for MI355X.
+
+The compute lives in ``libfe.so`` (hand-written HIP for gfx950 behind a C ABI
+declared in ``include/fe.h``).  :mod:`.binding` marshals torch tensors into
+those calls; the library is loaded on first use and a missing or unbuilt
+library is an error -- there is no CPU fallback.
+"""
+from .binding import (  # noqa: F401
+    fe_last_error,
+    fe_paged_gqa_decode,
+    fe_paged_gqa_decode_num_partitions,
+    fe_paged_gqa_decode_workspace_size,
+    fe_paged_gqa_prefill_chunk,
+    fe_paged_kv_append,
+    fe_status_string,
+    library_path,
+    load_library,
+)

@@ -1,0 +1,155 @@
+"""ctypes binding of libfe.so -- argument marshalling only.
+
+Each function has the name of the C entry point it calls (declared in
+``include/fe.h``), takes torch tensors, checks dtype/device/contiguity,
+passes ``data_ptr()`` and the current HIP stream, and raises
+:class:`FeError` on a non-zero status.  All arithmetic happens in the HIP
+kernels; if the library is not built this module raises instead of computing
+anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfe.so"
+_lib = None
+
+
+class FeError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func} failed: {fe_status_string(status)} ({status}): {detail}")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load libfe.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fe_paged_kv_append.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+    lib.fe_paged_kv_append.restype = I
+    lib.fe_paged_gqa_decode_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.fe_paged_gqa_decode_workspace_size.restype = Z
+    lib.fe_paged_gqa_decode_num_partitions.argtypes = [I, I, I, I, I, I]
+    lib.fe_paged_gqa_decode_num_partitions.restype = I
+    lib.fe_paged_gqa_decode.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.fe_paged_gqa_decode.restype = I
+    lib.fe_paged_gqa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, P]
+    lib.fe_paged_gqa_prefill_chunk.restype = I
+    lib.fe_status_string.argtypes = [I]
+    lib.fe_status_string.restype = ctypes.c_char_p
+    lib.fe_last_error.argtypes = []
+    lib.fe_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fe_status_string(status: int) -> str:
+    return load_library().fe_status_string(int(status)).decode()
+
+
+def fe_last_error() -> str:
+    return load_library().fe_last_error().decode()
+
+
+def _check(rc: int, func: str):
+    if rc != 0:
+        raise FeError(rc, func, fe_last_error())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name: str, ndim: Optional[int] = None):
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def fe_paged_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Scatter k_new/v_new [T][Hkv][D] into the pools [NB][Hkv][BS][D] by slot."""
+    NB, Hkv, BS, D = k_cache.shape
+    T = slot_mapping.shape[0]
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache shapes differ")
+    if T and (tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D)):
+        raise ValueError("k_new/v_new must be [T][Hkv][D]")
+    rc = load_library().fe_paged_kv_append(
+        _dev(k_new, torch.bfloat16, "k_new"), _dev(v_new, torch.bfloat16, "v_new"),
+        _dev(slot_mapping, torch.int32, "slot_mapping", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
+        _dev(v_cache, torch.bfloat16, "v_cache", 4), T, NB, Hkv, D, BS, _stream(stream))
+    _check(rc, "fe_paged_kv_append")
+
+
+def fe_paged_gqa_decode_workspace_size(B, Hq, Hkv, D, max_context_len, num_partitions=0) -> int:
+    n = load_library().fe_paged_gqa_decode_workspace_size(B, Hq, Hkv, D, max_context_len, num_partitions)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("fe_paged_gqa_decode_workspace_size: invalid sizes")
+    return int(n)
+
+
+def fe_paged_gqa_decode_num_partitions(B, Hq, Hkv, D, max_context_len, num_partitions=0) -> int:
+    n = load_library().fe_paged_gqa_decode_num_partitions(B, Hq, Hkv, D, max_context_len, num_partitions)
+    if n < 0:
+        raise ValueError("fe_paged_gqa_decode_num_partitions: invalid sizes")
+    return int(n)
+
+
+def fe_paged_gqa_decode(out, lse, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                        scale: float, num_partitions: int = 0, workspace=None, stream=None) -> None:
+    """Decode attention; ``workspace`` (uint8 device tensor) is allocated by
+    torch when not given."""
+    B, Hq, D = q.shape
+    NB, Hkv, BS, _ = k_cache.shape
+    ws_bytes = fe_paged_gqa_decode_workspace_size(B, Hq, Hkv, D, max_context_len, num_partitions)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, torch.uint8, "workspace") if workspace is not None else None
+    ws_have = workspace.numel() if workspace is not None else 0
+    rc = load_library().fe_paged_gqa_decode(
+        _dev(out, torch.bfloat16, "out", 3), _dev(lse, torch.float32, "lse", 2), _dev(q, torch.bfloat16, "q", 3),
+        _dev(k_cache, torch.bfloat16, "k_cache", 4), _dev(v_cache, torch.bfloat16, "v_cache", 4),
+        _dev(block_tables, torch.int32, "block_tables", 2), block_tables.shape[1],
+        _dev(context_lens, torch.int32, "context_lens", 1), B, Hq, Hkv, D, BS, NB, int(max_context_len),
+        float(scale), int(num_partitions), ws_ptr, ws_have, _stream(stream))
+    _check(rc, "fe_paged_gqa_decode")
+
+
+def fe_paged_gqa_prefill_chunk(out, lse, q, query_start_loc, k_cache, v_cache, block_tables, context_lens,
+                               max_q_len: int, max_context_len: int, scale: float, stream=None) -> None:
+    """Chunked prefill attention over the paged cache (bottom-right causal)."""
+    total_q, Hq, D = q.shape
+    NB, Hkv, BS, _ = k_cache.shape
+    B = context_lens.shape[0]
+    rc = load_library().fe_paged_gqa_prefill_chunk(
+        _dev(out, torch.bfloat16, "out", 3), _dev(lse, torch.float32, "lse", 2), _dev(q, torch.bfloat16, "q", 3),
+        _dev(query_start_loc, torch.int32, "query_start_loc", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
+        _dev(v_cache, torch.bfloat16, "v_cache", 4), _dev(block_tables, torch.int32, "block_tables", 2),
+        block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens", 1), B, total_q, int(max_q_len),
+        Hq, Hkv, D, BS, NB, int(max_context_len), float(scale), _stream(stream))
+    _check(rc, "fe_paged_gqa_prefill_chunk")

@@ -1,0 +1,250 @@
+"""Seeded synthetic workloads for paged GQA attention.
+
+This module only builds inputs: sequence lengths, block placement in a shared
+pool, bf16 query/key/value values, slot mappings and poison fill.  It holds
+none of the attention arithmetic and imports neither the HIP binding nor the
+oracle, so both sides can be fed the same bytes.
+
+The shapes are the Qwen3 layer shapes of the two models the pages run --
+Qwen3-0.6B in "Make the Engine Talk" section 1.1, Qwen3-4B-Instruct-2507 in
+the ForgeEngine README -- at head_dim 128 and 16-token KV blocks.  The pages
+name no benchmark data set; values are N(0, 1) drawn from torch's CPU
+generator and rounded to bf16 (round to nearest even).
+
+Layout (shared by every workload):
+  * K and V pools: bf16 [num_blocks][Hkv][16][128], head-major inside a block;
+  * block_tables: int32 [B][max_blocks_per_seq]; entries past a sequence's
+    last block point at a dedicated poisoned block;
+  * slot = block * 16 + offset (int32); context_lens[b] counts the tokens
+    appended this step;
+  * every pool slot that holds no token -- unused blocks, tail slots of a
+    sequence's last block, the slots appended tokens will fill -- holds poison
+    (a large finite bf16 value, or NaN).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+D = 128
+BS = 16
+POISON_LARGE = 30000.0
+
+
+def fp32_scale(head_dim: int = D) -> float:
+    """1/sqrt(head_dim) rounded to fp32 (the value every call receives)."""
+    return float(np.float32(1.0 / math.sqrt(head_dim)))
+
+
+# Stream ids: every random quantity gets its own generator so that changing
+# one size does not shift the others.
+_LEN, _PERM, _Q, _K, _V, _SPIKE = 1, 2, 3, 4, 5, 6
+
+
+def _gen(seed: int, stream: int, layer: int = 0) -> torch.Generator:
+    return torch.Generator().manual_seed(seed * 100003 + layer * 101 + stream)
+
+
+@dataclass
+class Spec:
+    """Shape recipe of one workload."""
+
+    name: str
+    kind: str  # "decode" or "prefill"
+    B: int
+    Hq: int
+    Hkv: int
+    len_lo: int  # context length range (inclusive), counting appended tokens
+    len_hi: int
+    append: int = 0  # tokens appended per sequence before attention
+    layers: int = 1  # independent pools (one decode call each)
+    pool_blocks: Optional[int] = None  # fixed pool size, else 1.125 x needed
+    spike_frac: float = 0.0  # fraction of token positions whose K is x spike_mul
+    spike_mul: float = 3.0
+    chunk: int = 0  # prefill query chunk per sequence (bottom-right causal)
+
+
+# The five workloads.  Names state the model shape and the sizes.
+SPECS = {
+    # Qwen3-0.6B layer (16 q heads, 8 KV heads, G = 2): one sequence of 128
+    # tokens in 8 blocks of a 64-block pool; 1 token appended first.
+    "qwen3_0.6b_b1_ctx128": Spec("qwen3_0.6b_b1_ctx128", "decode", 1, 16, 8, 128, 128, append=1,
+                                 pool_blocks=64),
+    # Qwen3-4B layer (32/8, G = 4), 4 sequences of 256..2048 tokens, 36 layers
+    # with independent pools sharing one block table: one step = 36 calls.
+    "qwen3_4b_b4_ctx256-2048_36layers": Spec("qwen3_4b_b4_ctx256-2048_36layers", "decode", 4, 32, 8, 256,
+                                             2048, layers=36),
+    # Qwen3-4B, 64 sequences of 1024..8192 tokens; K x3 on 1% of positions;
+    # 1 token appended per sequence first.
+    "qwen3_4b_b64_ctx1024-8192": Spec("qwen3_4b_b64_ctx1024-8192", "decode", 64, 32, 8, 1024, 8192,
+                                      append=1, spike_frac=0.01),
+    # Qwen3-4B long context: 8 sequences of 32768 tokens (split-K).
+    "qwen3_4b_b8_ctx32768": Spec("qwen3_4b_b8_ctx32768", "decode", 8, 32, 8, 32768, 32768),
+    # Qwen3-4B chunked prefill: 4 sequences of 4096 cached + 256 new tokens;
+    # the 256-token chunks are appended, then attend causally.
+    "qwen3_4b_b4_prefix4096_chunk256": Spec("qwen3_4b_b4_prefix4096_chunk256", "prefill", 4, 32, 8, 4352,
+                                            4352, append=256, chunk=256),
+}
+ORDER = list(SPECS)  # default seed of SPECS[ORDER[i]] is i + 1
+
+
+@dataclass
+class Layer:
+    k_cache: torch.Tensor  # bf16 [NB][Hkv][BS][D], before the append
+    v_cache: torch.Tensor
+    q: torch.Tensor  # bf16 [B][Hq][D] (decode) or [total_q][Hq][D] (prefill)
+    k_new: torch.Tensor  # bf16 [T][Hkv][D]
+    v_new: torch.Tensor
+    k_seq: Optional[torch.Tensor] = None  # bf16 [sum L][Hkv][D], contiguous copy
+    v_seq: Optional[torch.Tensor] = None
+
+
+@dataclass
+class Workload:
+    spec: Spec
+    seed: int
+    scale: float
+    num_blocks: int
+    context_lens: torch.Tensor  # int32 [B]
+    block_tables: torch.Tensor  # int32 [B][max_blocks_per_seq]
+    slot_mapping: torch.Tensor  # int32 [T]
+    query_start_loc: Optional[torch.Tensor]  # int32 [B+1] (prefill)
+    poison_block: int
+    layers: list = field(default_factory=list)
+
+    @property
+    def B(self):
+        return self.spec.B
+
+    @property
+    def Hq(self):
+        return self.spec.Hq
+
+    @property
+    def Hkv(self):
+        return self.spec.Hkv
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max().item()) if self.context_lens.numel() else 0
+
+    @property
+    def kv_tokens(self) -> int:
+        return int(self.context_lens.sum().item())
+
+    @property
+    def seq_offsets(self) -> list:
+        lens = self.context_lens.tolist()
+        return [0] + list(np.cumsum(lens))
+
+
+def _poison_value(poison: str) -> float:
+    if poison == "large":
+        return POISON_LARGE
+    if poison == "nan":
+        return float("nan")
+    raise ValueError(poison)
+
+
+def build(spec: Spec, seed: int, poison: str = "large", keep_contiguous: bool = False,
+          lens: Optional[list] = None, layers: Optional[int] = None) -> Workload:
+    """Generate one workload.  ``lens`` overrides the drawn context lengths
+    (tests use it for edge cases); ``layers`` limits the number of pools."""
+    B = spec.B
+    if lens is None:
+        if spec.len_lo == spec.len_hi:
+            lens_t = torch.full((B,), spec.len_lo, dtype=torch.int64)
+        else:
+            lens_t = torch.randint(spec.len_lo, spec.len_hi + 1, (B,), generator=_gen(seed, _LEN))
+    else:
+        lens_t = torch.tensor(list(lens), dtype=torch.int64)
+        assert lens_t.numel() == B
+    lens_l = [int(x) for x in lens_t.tolist()]
+    append = spec.append
+    nblk = [(L + BS - 1) // BS for L in lens_l]
+    need = sum(nblk)
+    if spec.pool_blocks is not None:
+        NB = spec.pool_blocks
+    else:
+        NB = max(math.ceil(1.125 * need), need + 1)
+    assert NB >= need + 1, "pool must keep one block for poison"
+    perm = torch.randperm(NB, generator=_gen(seed, _PERM))
+    max_blocks = max(1, max(nblk) if nblk else 1)
+    poison_block = int(perm[need])
+    bt = torch.full((B, max_blocks), poison_block, dtype=torch.int64)
+    off = 0
+    for b in range(B):
+        bt[b, : nblk[b]] = perm[off : off + nblk[b]]
+        off += nblk[b]
+
+    # slot of every token, in sequence order; the last `append` tokens of each
+    # sequence are the new ones (clamped for sequences shorter than that)
+    tok_b = torch.repeat_interleave(torch.arange(B), torch.tensor(lens_l, dtype=torch.int64))
+    tok_t = torch.cat([torch.arange(L) for L in lens_l]) if lens_l and sum(lens_l) else torch.zeros(0, dtype=torch.int64)
+    tok_blk = bt[tok_b, tok_t // BS] if tok_t.numel() else tok_t
+    tok_off = tok_t % BS
+    is_new = torch.zeros(tok_t.shape, dtype=torch.bool)
+    for b in range(B):
+        a = min(append, lens_l[b])
+        if a:
+            start = sum(lens_l[:b])
+            is_new[start + lens_l[b] - a : start + lens_l[b]] = True
+    slot_mapping = (tok_blk * BS + tok_off)[is_new].to(torch.int32)
+
+    qsl = None
+    total_q = B
+    if spec.kind == "prefill":
+        chunks = [min(spec.chunk, L) for L in lens_l]
+        qsl = torch.tensor([0] + list(np.cumsum(chunks)), dtype=torch.int32)
+        total_q = int(qsl[-1])
+
+    pv = _poison_value(poison)
+    n_layers = spec.layers if layers is None else layers
+    out_layers = []
+    n_tok = tok_t.numel()
+    for layer in range(n_layers):
+        k = torch.randn((n_tok, spec.Hkv, D), generator=_gen(seed, _K, layer), dtype=torch.float32)
+        if spec.spike_frac > 0 and n_tok:
+            spike = torch.rand((n_tok,), generator=_gen(seed, _SPIKE, layer)) < spec.spike_frac
+            k[spike] *= spec.spike_mul
+        k = k.to(torch.bfloat16)
+        v = torch.randn((n_tok, spec.Hkv, D), generator=_gen(seed, _V, layer), dtype=torch.float32).to(
+            torch.bfloat16)
+        q = torch.randn((total_q, spec.Hq, D), generator=_gen(seed, _Q, layer), dtype=torch.float32).to(
+            torch.bfloat16)
+        kc = torch.full((NB, spec.Hkv, BS, D), pv, dtype=torch.bfloat16)
+        vc = torch.full((NB, spec.Hkv, BS, D), pv, dtype=torch.bfloat16)
+        old = ~is_new
+        # [NB][Hkv][BS][D] viewed as [NB][BS][Hkv][D] so (block, offset) indexes a token row
+        kc.permute(0, 2, 1, 3)[tok_blk[old], tok_off[old]] = k[old]
+        vc.permute(0, 2, 1, 3)[tok_blk[old], tok_off[old]] = v[old]
+        out_layers.append(Layer(
+            k_cache=kc, v_cache=vc, q=q,
+            k_new=k[is_new].contiguous(), v_new=v[is_new].contiguous(),
+            k_seq=k if keep_contiguous else None, v_seq=v if keep_contiguous else None))
+        del k, v
+    return Workload(spec=spec, seed=seed, scale=fp32_scale(D), num_blocks=NB,
+                    context_lens=torch.tensor(lens_l, dtype=torch.int32),
+                    block_tables=bt.to(torch.int32), slot_mapping=slot_mapping, query_start_loc=qsl,
+                    poison_block=poison_block, layers=out_layers)
+
+
+def make(name: str, seed: Optional[int] = None, **kw) -> Workload:
+    """Workload by name; the default seed is the workload's 1-based position."""
+    if seed is None:
+        seed = ORDER.index(name) + 1
+    return build(SPECS[name], seed, **kw)
+
+
+def custom(kind: str, B: int, Hq: int, Hkv: int, lens, seed: int, append: int = 0, chunk: int = 0,
+           spike_frac: float = 0.0, pool_blocks: Optional[int] = None, layers: int = 1, **kw) -> Workload:
+    """Ad-hoc workload with explicit lengths (edge cases, small parity sizes)."""
+    lens = list(lens)
+    spec = Spec(f"custom_{kind}_b{B}_h{Hq}x{Hkv}", kind, B, Hq, Hkv, min(lens) if lens else 0,
+                max(lens) if lens else 0, append=append, layers=layers, pool_blocks=pool_blocks,
+                spike_frac=spike_frac, chunk=chunk)
+    return build(spec, seed, lens=lens, **kw)
