@@ -1,0 +1,225 @@
+"""Benchmark of the paged GQA hot path on one MI355X.
+
+One step = the whole decode hot path over one batch: KV append of the new
+token of every sequence (fe_paged_kv_append), then paged GQA decode
+(fe_paged_gqa_decode: split-K pass 1 + LSE merge).  Inputs are resident in HBM
+before timing starts.  The default workload is the Qwen3-4B layer shape at
+serving concurrency: 64 sequences, 32 query / 8 KV heads, head_dim 128, 16-token
+blocks, context lengths 1024..8192 (seeded, synthetic).
+
+Prints one JSON line.  `value` is algorithmic HBM bytes per step / step time
+in GB/s; `roofline` is for the decode call, timed with HIP events on the
+stream its kernels run on; `cpu_baseline` is the fp64 oracle on the host.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA peak
+DEFAULT_WORKLOAD = "qwen3_4b_b64_ctx1024-8192"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic HBM bytes of one decode call: K and V of every attended
+    token and KV head, q, out, lse, block ids and context lengths."""
+    lens = [int(x) for x in w.context_lens.tolist()]
+    kv = sum(lens) * w.Hkv * 128 * 2 * 2
+    blocks = sum((L + 15) // 16 for L in lens)
+    return kv + w.B * w.Hq * 128 * 2 * 2 + w.B * w.Hq * 4 + blocks * 4 + w.B * 4
+
+
+def append_bytes(w) -> int:
+    T = int(w.slot_mapping.numel())
+    return T * w.Hkv * 128 * 2 * 2 * 2 + T * 4  # read new K/V, write into the pools, slots
+
+
+def prefill_flops(w) -> int:
+    """4*D flop per unmasked (query, key, head) triple (QK^T and PV)."""
+    qsl = w.query_start_loc.tolist()
+    tot = 0
+    for b, L in enumerate(w.context_lens.tolist()):
+        C = qsl[b + 1] - qsl[b]
+        tot += sum(L - C + i + 1 for i in range(C))
+    return tot * w.Hq * 4 * 128
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle (as it stands) on the host cores."""
+    import oracle
+
+    lay = w.layers[0]
+    rk, rv = oracle.append(lay.k_new, lay.v_new, w.slot_mapping, lay.k_cache, lay.v_cache)
+    threads = os.cpu_count() or 1
+    if w.spec.kind == "decode":
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.decode(lay.q, rk, rv, w.block_tables, w.context_lens, w.scale, nthreads=threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 50:
+                break
+        per = el / reps
+        return {"value": round(decode_bytes(w) / per / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": f"fp64 oracle decode over the full workload ({w.kv_tokens} KV tokens x {w.Hkv} KV heads), "
+                          f"{reps} repetitions, {per * 1e3:.1f} ms each; append not included",
+                "kv_tokens_per_s": round(w.kv_tokens / per, 1)}
+    # prefill: a bounded sample of packed rows, scaled to the whole chunk
+    total_q = lay.q.shape[0]
+    n = max(1, min(total_q, 64))
+    rows = list(range(0, total_q, max(1, total_q // n)))[:n]
+    t0 = time.perf_counter()
+    oracle.prefill_chunk(lay.q, w.query_start_loc, rk, rv, w.block_tables, w.context_lens, w.scale, rows=rows,
+                         nthreads=threads)
+    el = time.perf_counter() - t0
+    frac = len(rows) / total_q
+    return {"value": round(prefill_flops(w) * frac / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "sample": f"fp64 oracle prefill on {len(rows)} of {total_q} query rows ({el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--partitions", type=int, default=0, help="decode split-K factor (0 = automatic)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_gqa_slot_amd as fe
+    from paged_kv_gqa_slot_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    fe.load_library()
+    log(f"generating workload {args.workload} ...")
+    w = inputs.make(args.workload, seed=args.seed)
+    spec = w.spec
+    log(f"  B={w.B} Hq={w.Hq} Hkv={w.Hkv} layers={len(w.layers)} kv_tokens={w.kv_tokens} pool={w.num_blocks} blocks")
+
+    L = [dict(kc=l.k_cache.to(dev), vc=l.v_cache.to(dev), q=l.q.to(dev), kn=l.k_new.to(dev), vn=l.v_new.to(dev))
+         for l in w.layers]
+    slots = w.slot_mapping.to(dev)
+    bt = w.block_tables.to(dev)
+    lens = w.context_lens.to(dev)
+    qsl = w.query_start_loc.to(dev) if w.query_start_loc is not None else None
+    mcl = w.max_context_len
+    total_q = L[0]["q"].shape[0]
+    out = torch.empty(total_q, w.Hq, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(total_q, w.Hq, dtype=torch.float32, device=dev)
+    is_decode = spec.kind == "decode"
+    P = fe.fe_paged_gqa_decode_num_partitions(w.B, w.Hq, w.Hkv, 128, mcl, args.partitions) if is_decode else 0
+    ws_bytes = fe.fe_paged_gqa_decode_workspace_size(w.B, w.Hq, w.Hkv, 128, mcl, args.partitions) if is_decode else 0
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    max_q = max(b - a for a, b in zip(w.query_start_loc.tolist()[:-1], w.query_start_loc.tolist()[1:])) if qsl is not None else 0
+    do_append = slots.numel() > 0
+
+    def attend(x):
+        if is_decode:
+            fe.fe_paged_gqa_decode(out, lse, x["q"], x["kc"], x["vc"], bt, lens, mcl, w.scale,
+                                   num_partitions=args.partitions, workspace=ws)
+        else:
+            fe.fe_paged_gqa_prefill_chunk(out, lse, x["q"], qsl, x["kc"], x["vc"], bt, lens, max_q, mcl, w.scale)
+
+    def step():
+        for x in L:
+            if do_append:
+                fe.fe_paged_kv_append(x["kn"], x["vn"], slots, x["kc"], x["vc"])
+            attend(x)
+
+    log(f"warmup {args.warmup} steps (partitions={P}, workspace={ws_bytes} B)")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel timing of the attention call (the dominant kernel), same stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        for x in L:
+            if do_append:
+                fe.fe_paged_kv_append(x["kn"], x["vn"], slots, x["kc"], x["vc"])
+        a.record(stream)
+        for x in L:
+            attend(x)
+        b.record(stream)
+    torch.cuda.synchronize()
+    att_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    att_avg_ms = sum(att_ms) / len(att_ms) / len(L)
+    att_med_ms = att_ms[len(att_ms) // 2] / len(L)
+
+    nl = len(L)
+    if is_decode:
+        att_bytes = decode_bytes(w)
+        step_bytes = nl * (att_bytes + (append_bytes(w) if do_append else 0))
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+        achieved = att_bytes / (att_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "fe_paged_gqa_decode (gqa_decode_partition_kernel + gqa_decode_merge_kernel)"
+                          if P > 1 else "fe_paged_gqa_decode (gqa_decode_partition_kernel)",
+                "per_launch_bytes": att_bytes, "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5)}
+        metric = "paged GQA decode achieved HBM GB/s (% of peak) + KV tokens/s, Qwen3-4B shape"
+        unit = "GB/s"
+        extra = {"pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                 "kv_tokens_per_s": round(nl * w.kv_tokens / (ms_per_step * 1e-3), 1),
+                 "decode_only_kv_tokens_per_s": round(w.kv_tokens / (att_avg_ms * 1e-3), 1)}
+    else:
+        flops = prefill_flops(w)
+        value = nl * flops / (ms_per_step * 1e-3) / 1e12
+        achieved = flops / (att_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                "kernel": "fe_paged_gqa_prefill_chunk (gqa_prefill_chunk_kernel)", "per_launch_flops": flops,
+                "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5)}
+        metric = "paged GQA chunked-prefill TFLOP/s (% of bf16 MFMA peak), Qwen3-4B shape"
+        unit = "TFLOP/s"
+        extra = {}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline ...")
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    cfg = {"workload": spec.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": 128,
+           "block_size": 16, "layers": nl, "kv_tokens": w.kv_tokens, "max_context_len": mcl,
+           "append_tokens_per_step": int(slots.numel()) * nl, "num_partitions": P, "seed": w.seed}
+    rec = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg, **extra, "roofline": roof,
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+// C ABI of libfe.so (declared in include/fe.h): synchronous argument checks,
+// then asynchronous kernel launches on the caller's stream.  Nothing here
+// allocates, and no C++ exception leaves these functions.
+#include "fe.h"
+
+#include <math.h>
+
+#include <cstdio>
+#include <string>
+
+#include "fe_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* func, const char* what) {
+  char buf[512];
+  std::snprintf(buf, sizeof buf, "%s: %s", func, what);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* func) {
+  char buf[512];
+  std::snprintf(buf, sizeof buf, "%s: HIP error %d (%s)", func, static_cast<int>(e), hipGetErrorString(e));
+  g_last_error = buf;
+  return FE_ERR_HIP;
+}
+
+// Shape checks shared by the attention calls.  Returns FE_OK or an error
+// status (with the message recorded).
+int check_heads(const char* func, int Hq, int Hkv, int D, int BS) {
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0) return fail(FE_ERR_INVALID_ARG, func, "Hq, Hkv, D and BS must be positive");
+  if (Hq % Hkv != 0) return fail(FE_ERR_INVALID_ARG, func, "Hq must be a multiple of Hkv");
+  if (D != fe::kHeadDim) return fail(FE_ERR_UNSUPPORTED, func, "only head_dim 128 is built");
+  if (BS != fe::kBlockSize) return fail(FE_ERR_UNSUPPORTED, func, "only KV block size 16 is built");
+  if (Hq / Hkv > 8) return fail(FE_ERR_UNSUPPORTED, func, "group size Hq/Hkv above 8 is not built");
+  return FE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fe_status_string(int status) {
+  switch (status) {
+    case FE_OK: return "FE_OK";
+    case FE_ERR_NULL: return "FE_ERR_NULL";
+    case FE_ERR_INVALID_ARG: return "FE_ERR_INVALID_ARG";
+    case FE_ERR_UNSUPPORTED: return "FE_ERR_UNSUPPORTED";
+    case FE_ERR_WORKSPACE: return "FE_ERR_WORKSPACE";
+    case FE_ERR_HIP: return "FE_ERR_HIP";
+    case FE_ERR_INTERNAL: return "FE_ERR_INTERNAL";
+    default: return "FE_ERR_UNKNOWN";
+  }
+}
+
+const char* fe_last_error(void) { return g_last_error.c_str(); }
+
+int fe_paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_cache,
+                       void* v_cache, int T, int num_blocks, int Hkv, int D, int BS, hipStream_t stream) {
+  static const char* fn = "fe_paged_kv_append";
+  try {
+    if (T < 0 || num_blocks <= 0 || Hkv <= 0 || D <= 0 || BS <= 0)
+      return fail(FE_ERR_INVALID_ARG, fn, "T must be >= 0 and num_blocks, Hkv, D, BS positive");
+    if (D != fe::kHeadDim) return fail(FE_ERR_UNSUPPORTED, fn, "only head_dim 128 is built");
+    if (BS != fe::kBlockSize) return fail(FE_ERR_UNSUPPORTED, fn, "only KV block size 16 is built");
+    if (!k_cache || !v_cache) return fail(FE_ERR_NULL, fn, "k_cache and v_cache must not be NULL");
+    if (T == 0) return FE_OK;
+    if (!k_new || !v_new || !slot_mapping) return fail(FE_ERR_NULL, fn, "k_new, v_new, slot_mapping must not be NULL");
+    const hipError_t e = fe::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, T, num_blocks, Hkv, stream);
+    return e == hipSuccess ? FE_OK : hip_fail(e, fn);
+  } catch (...) {
+    return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
+  }
+}
+
+size_t fe_paged_gqa_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len, int num_partitions) {
+  fe::DecodePlan plan;
+  if (D != fe::kHeadDim || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0) return static_cast<size_t>(-1);
+  if (!fe::plan_decode(B, Hq, Hkv, max_context_len, num_partitions, &plan)) return static_cast<size_t>(-1);
+  return plan.workspace_bytes;
+}
+
+int fe_paged_gqa_decode_num_partitions(int B, int Hq, int Hkv, int D, int max_context_len, int num_partitions) {
+  fe::DecodePlan plan;
+  if (D != fe::kHeadDim || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0) return -1;
+  if (!fe::plan_decode(B, Hq, Hkv, max_context_len, num_partitions, &plan)) return -1;
+  return plan.partitions;
+}
+
+int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens, int B,
+                        int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale,
+                        int num_partitions, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  static const char* fn = "fe_paged_gqa_decode";
+  try {
+    if (B < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_partitions < 0)
+      return fail(FE_ERR_INVALID_ARG, fn,
+                  "B, max_context_len, num_partitions must be >= 0; num_blocks, max_blocks_per_seq positive");
+    if (int rc = check_heads(fn, Hq, Hkv, D, BS)) return rc;
+    if (!isfinite(scale)) return fail(FE_ERR_INVALID_ARG, fn, "scale must be finite");
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+      return fail(FE_ERR_NULL, fn, "out, q, k_cache, v_cache, block_tables, context_lens must not be NULL");
+    fe::DecodePlan plan;
+    if (!fe::plan_decode(B, Hq, Hkv, max_context_len, num_partitions, &plan))
+      return fail(FE_ERR_INVALID_ARG, fn, "cannot plan these sizes");
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+      return fail(FE_ERR_WORKSPACE, fn, "workspace missing or smaller than fe_paged_gqa_decode_workspace_size()");
+    if (B == 0) return FE_OK;
+    fe::DecodeArgs a{out, lse, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv,
+                     num_blocks, max_context_len, scale, plan, workspace};
+    const hipError_t e = fe::launch_decode(a, stream);
+    return e == hipSuccess ? FE_OK : hip_fail(e, fn);
+  } catch (...) {
+    return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
+  }
+}
+
+int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32_t* query_start_loc,
+                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                               int max_blocks_per_seq, const int32_t* context_lens, int B, int total_q, int max_q_len,
+                               int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale,
+                               hipStream_t stream) {
+  static const char* fn = "fe_paged_gqa_prefill_chunk";
+  try {
+    if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+      return fail(FE_ERR_INVALID_ARG, fn,
+                  "B, total_q, max_q_len, max_context_len must be >= 0; num_blocks, max_blocks_per_seq positive");
+    if (int rc = check_heads(fn, Hq, Hkv, D, BS)) return rc;
+    if (!isfinite(scale)) return fail(FE_ERR_INVALID_ARG, fn, "scale must be finite");
+    if (B == 0 || total_q == 0) return FE_OK;
+    if (!out || !q || !query_start_loc || !k_cache || !v_cache || !block_tables || !context_lens)
+      return fail(FE_ERR_NULL, fn,
+                  "out, q, query_start_loc, k_cache, v_cache, block_tables, context_lens must not be NULL");
+    fe::PrefillArgs a{out, lse, q, query_start_loc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                      B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale};
+    const hipError_t e = fe::launch_prefill(a, stream);
+    return e == hipSuccess ? FE_OK : hip_fail(e, fn);
+  } catch (...) {
+    return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: libfe.so loads, exports every function
+include/fe.h declares, and rejects bad arguments synchronously (before any
+HIP call) with the documented status codes.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_gqa_slot_amd as fe
+from paged_kv_gqa_slot_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fe.h")
+
+OK, NULL, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3, -4
+P = 0x1000  # a non-NULL placeholder pointer: never dereferenced on these paths
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.skip("libfe.so not built")
+    return fe.load_library()
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("fe_paged_kv_append", "fe_paged_gqa_decode", "fe_paged_gqa_prefill_chunk",
+              "fe_paged_gqa_decode_workspace_size", "fe_status_string", "fe_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libfe.so does not export {name}"
+
+
+def test_python_binding_has_same_names():
+    for name in declared_functions():
+        assert hasattr(fe, name) or hasattr(binding, name), name
+
+
+def test_status_strings(lib):
+    assert fe.fe_status_string(0) == "FE_OK"
+    assert fe.fe_status_string(-4) == "FE_ERR_WORKSPACE"
+    assert fe.fe_status_string(12345) == "FE_ERR_UNKNOWN"
+
+
+def dec(lib, **kw):
+    a = dict(out=P, lse=None, q=P, k=P, v=P, bt=P, mb=8, cl=P, B=2, Hq=32, Hkv=8, D=128, BS=16, NB=64, mcl=128,
+             scale=0.088, parts=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.fe_paged_gqa_decode(a["out"], a["lse"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["cl"], a["B"],
+                                   a["Hq"], a["Hkv"], a["D"], a["BS"], a["NB"], a["mcl"], a["scale"], a["parts"],
+                                   a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_argument_errors(lib):
+    assert dec(lib, q=None) == NULL
+    assert dec(lib, out=None) == NULL
+    assert dec(lib, bt=None) == NULL
+    assert dec(lib, Hq=30) == INVALID  # not a multiple of Hkv
+    assert dec(lib, Hkv=0) == INVALID
+    assert dec(lib, B=-1) == INVALID
+    assert dec(lib, NB=0) == INVALID
+    assert dec(lib, mcl=-5) == INVALID
+    assert dec(lib, parts=-1) == INVALID
+    assert dec(lib, scale=float("nan")) == INVALID
+    assert dec(lib, scale=float("inf")) == INVALID
+    assert dec(lib, D=64) == UNSUPPORTED
+    assert dec(lib, BS=32) == UNSUPPORTED
+    assert dec(lib, Hq=72, Hkv=8) == UNSUPPORTED  # G = 9
+    assert "head_dim" in fe.fe_last_error() or dec(lib, D=64) == UNSUPPORTED
+    assert dec(lib, D=64) == UNSUPPORTED and "head_dim 128" in fe.fe_last_error()
+    # split-K needs a workspace of the queried size
+    need = lib.fe_paged_gqa_decode_workspace_size(2, 32, 8, 128, 4096, 8)
+    assert need > 0
+    assert dec(lib, mcl=4096, mb=256, parts=8) == WORKSPACE
+    assert dec(lib, mcl=4096, mb=256, parts=8, ws=P, wsb=need - 1) == WORKSPACE
+    assert "workspace" in fe.fe_last_error()
+
+
+def test_decode_batch_zero_is_noop(lib):
+    assert dec(lib, B=0) == OK
+
+
+def test_workspace_and_partition_queries(lib):
+    ws = lib.fe_paged_gqa_decode_workspace_size
+    npart = lib.fe_paged_gqa_decode_num_partitions
+    assert ws(2, 32, 8, 128, 4096, 1) == 0
+    assert npart(2, 32, 8, 128, 4096, 1) == 1
+    assert npart(8, 32, 8, 128, 32768, 8) == 8
+    assert npart(8, 32, 8, 128, 32768, 16) == 16
+    assert npart(8, 32, 8, 128, 32768, 32) == 32
+    # partitions never outnumber KV blocks
+    assert npart(1, 16, 8, 128, 40, 100) == 3
+    # the automatic choice depends only on the arguments and needs the queried workspace
+    p = npart(64, 32, 8, 128, 8192, 0)
+    assert p >= 1 and npart(64, 32, 8, 128, 8192, 0) == p
+    if p > 1:
+        assert ws(64, 32, 8, 128, 8192, 0) >= 64 * 32 * p * (128 + 1) * 4
+    assert ws(2, 32, 8, 64, 4096, 1) == ctypes.c_size_t(-1).value
+    assert npart(2, 30, 8, 128, 4096, 1) == -1
+    assert ws(2, 32, 8, 128, 0, 0) == 0
+
+
+def app(lib, **kw):
+    a = dict(kn=P, vn=P, sm=P, kc=P, vc=P, T=4, NB=64, Hkv=8, D=128, BS=16, stream=None)
+    a.update(kw)
+    return lib.fe_paged_kv_append(a["kn"], a["vn"], a["sm"], a["kc"], a["vc"], a["T"], a["NB"], a["Hkv"], a["D"],
+                                  a["BS"], a["stream"])
+
+
+def test_append_argument_errors(lib):
+    assert app(lib, kn=None) == NULL
+    assert app(lib, kc=None) == NULL
+    assert app(lib, sm=None) == NULL
+    assert app(lib, T=-1) == INVALID
+    assert app(lib, NB=0) == INVALID
+    assert app(lib, D=256) == UNSUPPORTED
+    assert app(lib, BS=8) == UNSUPPORTED
+    assert app(lib, T=0, kn=None, vn=None, sm=None) == OK  # nothing to do
+
+
+def pre(lib, **kw):
+    a = dict(out=P, lse=None, q=P, qsl=P, k=P, v=P, bt=P, mb=8, cl=P, B=2, tq=16, mql=8, Hq=32, Hkv=8, D=128, BS=16,
+             NB=64, mcl=128, scale=0.088, stream=None)
+    a.update(kw)
+    return lib.fe_paged_gqa_prefill_chunk(a["out"], a["lse"], a["q"], a["qsl"], a["k"], a["v"], a["bt"], a["mb"],
+                                          a["cl"], a["B"], a["tq"], a["mql"], a["Hq"], a["Hkv"], a["D"], a["BS"],
+                                          a["NB"], a["mcl"], a["scale"], a["stream"])
+
+
+def test_prefill_argument_errors(lib):
+    assert pre(lib, qsl=None) == NULL
+    assert pre(lib, q=None) == NULL
+    assert pre(lib, Hq=12) == INVALID
+    assert pre(lib, tq=-1) == INVALID
+    assert pre(lib, mql=-1) == INVALID
+    assert pre(lib, scale=float("nan")) == INVALID
+    assert pre(lib, D=96) == UNSUPPORTED
+    assert pre(lib, B=0) == OK
+    assert pre(lib, tq=0) == OK
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    q = torch.zeros(1, 16, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(4, 8, 16, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        fe.fe_paged_gqa_decode(torch.empty_like(q), None, q, kc, kc, torch.zeros(1, 4, dtype=torch.int32),
+                               torch.ones(1, dtype=torch.int32), 16, 0.088, num_partitions=1)
