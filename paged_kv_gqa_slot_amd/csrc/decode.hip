@@ -6,20 +6,23 @@
 // Pass 1 (gqa_decode_partition_kernel): one workgroup of 4 waves per
 // (sequence, KV head, partition of KV blocks).  Each wave takes every 4th
 // block of the partition and streams its K and V tiles (4 KiB each, one
-// contiguous run per (block, KV head)) straight into registers, one tile ahead
-// of the math.  A wave holds all G query heads of the group, so each K/V byte
-// is read from HBM once and used G times from registers.
+// contiguous run per (block, KV head)) straight into registers with
+// non-temporal loads, one tile ahead of the math.  A wave holds all G query
+// heads of the group, so each K/V byte is read from HBM once and used G times
+// from registers.
 //
-//   lane layout inside a wave: lane = 8 * grp + c.  The 8 lanes of a group
-//   share tokens grp and grp + 8 of every block; lane c holds dims
-//   [16c, 16c + 16).  QK^T: v_dot2_f32_bf16 on packed bf16 pairs, then a
-//   3-step DPP sum over the 8 lanes.  Each group keeps its own online-softmax
-//   state (running max m, sum l, acc[G][16]) in the log2 domain; the max is
-//   only raised when it grows by more than 8 (so exp2 stays <= 256 and the
-//   rescale of acc is rare).  PV: fp32 FMA on the unpacked V row.
+//   lane layout inside a wave: lane = 16 * r + c.  Load instruction j of a
+//   tile reads token rows 4j .. 4j + 3 as one contiguous 1 KiB run, so lane
+//   (r, c) holds dims [8c, 8c + 8) of tokens r, r + 4, r + 8, r + 12.
+//   QK^T: v_dot2_f32_bf16 on packed bf16 pairs, then a 4-step DPP sum over the
+//   16 lanes of a row.  Each row keeps its own online-softmax state (running
+//   max m, sum l, acc[G][8]) in the log2 domain; the max is only raised when
+//   it grows by more than 8 (so exp2 stays <= 256 and the rescale of acc is
+//   rare).  PV: fp32 FMA on the unpacked V row.  A partially filled last
+//   block is handled after the main loop by a masked variant of the same step.
 //
-// At the end the 8 groups and 4 waves are merged (max-shifted sums) through
-// DPP, cross-lane shuffles and LDS.  With one partition the kernel writes the
+// At the end the 4 rows and 4 waves are merged (max-shifted sums) through
+// cross-lane shuffles and LDS.  With one partition the kernel writes the
 // bf16 output and the LSE; otherwise it writes a normalised fp32 partial and
 // its LSE, and pass 2 (gqa_decode_merge_kernel) combines the partitions of a
 // row by log-sum-exp.
@@ -39,6 +42,10 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kTargetWorkgroups = 2048;  // automatic split-K aims for this many pass-1 workgroups
 constexpr int kMinPartBlocks = 8;        // ... but no partition shorter than 128 tokens
+#ifndef FE_DECODE_PREFETCH
+#define FE_DECODE_PREFETCH 1
+#endif
+constexpr int kPrefetch = FE_DECODE_PREFETCH;  // tiles in flight per wave beyond the one being consumed
 
 struct DecodeParams {
   const uint16_t* q;
@@ -58,71 +65,97 @@ struct DecodeParams {
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
 struct Tile {
-  uint4 k[4];  // tokens grp (k[0..1]) and grp + 8 (k[2..3]), dims [16c, 16c + 16)
+  uint4 k[4];  // k[j]: dims [8c, 8c + 8) of token 4j + r
   uint4 v[4];
 };
 
-__device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kbase, const uint16_t* vbase, int lane_vec) {
-  const uint4* kp = reinterpret_cast<const uint4*>(kbase) + lane_vec;
-  const uint4* vp = reinterpret_cast<const uint4*>(vbase) + lane_vec;
-  // token grp + 8 is 8 rows = 8 * 128 bf16 = 128 uint4 further on
-  t.k[0] = kp[0];
-  t.k[1] = kp[1];
-  t.k[2] = kp[128];
-  t.k[3] = kp[129];
-  t.v[0] = vp[0];
-  t.v[1] = vp[1];
-  t.v[2] = vp[128];
-  t.v[3] = vp[129];
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over one 4 KiB (block, KV head) tile.  Loads at offsets
+// >= num_bytes return zeros without touching memory, which masks whole
+// out-of-range tiles (num_bytes = 0) and the unused rows of a partial last
+// block (num_bytes = valid_tokens * 256) while every load instruction is
+// still issued unconditionally.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0), num_bytes,
+                                           0x00020000);
 }
 
-__device__ __forceinline__ void words(const uint4& a, const uint4& b, uint32_t (&w)[8]) {
+// Cache policy of the K/V loads: non-temporal (streamed, read once).
+constexpr int kLoadPolicyNT = 2;
+
+// Lane reads uint4 number lane + 64 j of the tile: instruction j fetches
+// token rows 4j .. 4j + 3 as one contiguous 1 KiB run.
+__device__ __forceinline__ void load_tile(Tile& t, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int lane) {
+  const int off = lane * 16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(kr, off + 1024 * j, 0, kLoadPolicyNT);
+    t.k[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(vr, off + 1024 * j, 0, kLoadPolicyNT);
+    t.v[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+__device__ __forceinline__ void words4(const uint4& a, uint32_t (&w)[4]) {
   w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+// Sum over each aligned group of 16 lanes (a DPP row); every lane gets it.
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppRowMirror>(x);
+  return x;
 }
 
 template <int G>
 struct State {
-  float m[G];
-  float l[G];
-  float acc[G][16];
+  float m[G];   // running max (log2 units), uniform within a row
+  float l[G];   // running sum of exp2(s - m), uniform within a row
+  float acc[G][8];
 };
 
-// Consume one 16-token tile.  `valid` holds, per token j of this lane's group
-// (t = grp + 8 j), whether it lies inside the context; `tail` is wave-uniform
-// and true only for a partially filled last block.
-template <int G>
-__device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint32_t (&qw)[G][8], float scale_log2,
-                                        bool tail, bool valid0, bool valid1) {
-  float s[2][G];
+// Consume one 16-token tile.  With kTail, tokens at or beyond `rem` (the
+// number of valid tokens in this block) are masked: their scores become -inf.
+// Their K/V words were already zeroed by the load's buffer range, so no slot
+// contents (NaN included) can reach acc through 0 * x.
+template <int G, bool kTail>
+__device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint32_t (&qw)[G][4], float scale_log2,
+                                        int r, int rem) {
+  float s[4][G];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    uint32_t kw[8];
-    words(t.k[2 * j], t.k[2 * j + 1], kw);
+  for (int j = 0; j < 4; ++j) {
+    uint32_t kw[4];
+    words4(t.k[j], kw);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a = dot2_bf16(qw[h][i], kw[i], a);
+      for (int i = 0; i < 4; ++i) a = dot2_bf16(qw[h][i], kw[i], a);
       s[j][h] = a;
     }
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[j][h] = sum8(s[j][h]) * scale_log2;
-  if (tail) {
+    for (int h = 0; h < G; ++h) s[j][h] = sum16(s[j][h]) * scale_log2;
+  if (kTail) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (!valid0) s[0][h] = -INFINITY;
-      if (!valid1) s[1][h] = -INFINITY;
-    }
+    for (int j = 0; j < 4; ++j)
+      if (4 * j + r >= rem)
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[j][h] = -INFINITY;
   }
   bool need = false;
   float mx[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    mx[h] = fmaxf(s[0][h], s[1][h]);
+    mx[h] = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
     need |= mx[h] > st.m[h] + kRescaleSlack;
   }
   if (__any(need)) {
@@ -133,28 +166,23 @@ __device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint3
         st.m[h] = mx[h];
         st.l[h] *= a;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st.acc[h][i] *= a;
+        for (int i = 0; i < 8; ++i) st.acc[h][i] *= a;
       }
     }
   }
-  float p[2][G];
+  float p[4][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    p[0][h] = fast_exp2(s[0][h] - st.m[h]);
-    p[1][h] = fast_exp2(s[1][h] - st.m[h]);
-    st.l[h] += p[0][h] + p[1][h];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j][h] = fast_exp2(s[j][h] - st.m[h]);
+    st.l[h] += (p[0][h] + p[1][h]) + (p[2][h] + p[3][h]);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    uint32_t vw[8];
-    words(t.v[2 * j], t.v[2 * j + 1], vw);
-    if (tail && !(j ? valid1 : valid0)) {
-      // never let a masked slot's contents (possibly NaN) reach acc via 0 * x
+  for (int j = 0; j < 4; ++j) {
+    uint32_t vw[4];
+    words4(t.v[j], vw);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) vw[i] = 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const float v0 = bf16_lo(vw[i]), v1 = bf16_hi(vw[i]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -166,7 +194,8 @@ __device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint3
 }
 
 template <int G>
-__global__ __launch_bounds__(kThreads) void gqa_decode_partition_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 2))) void gqa_decode_partition_kernel(
+    DecodeParams p) {
   __shared__ int s_bt[kMaxPartBlocks];
   __shared__ float s_o[kWaves][G][kHeadDim];
   __shared__ float s_m[kWaves][G];
@@ -175,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_partition_kernel(DecodePa
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int grp = lane >> 3, c = lane & 7;
+  const int r = lane >> 4, c = lane & 15;
 
   int wg = blockIdx.x;
   const int g = wg % p.Hkv;
@@ -188,16 +217,20 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_partition_kernel(DecodePa
   if (blk0 >= nblk && p.P > 1) return;  // nothing here; pass 2 never reads this partition
   const int blk1 = min(nblk, blk0 + p.part_blocks);
   const int nb = max(0, blk1 - blk0);
+  // tokens in the sequence's last block; that block is masked if partial
+  const int rem = L - (nblk - 1) * kBlockSize;
+  const bool has_tail = nb > 0 && blk1 == nblk && rem < kBlockSize;
+  const int nfull = nb - (has_tail ? 1 : 0);
 
   const int32_t* bt = p.block_tables + static_cast<size_t>(b) * p.max_blocks + blk0;
   for (int i = tid; i < nb; i += kThreads) s_bt[i] = min(max(bt[i], 0), p.num_blocks - 1);
 
   const size_t row0 = static_cast<size_t>(b) * p.Hq + static_cast<size_t>(g) * G;  // first q head of the group
-  uint32_t qw[G][8];
+  uint32_t qw[G][4];
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(p.q + row0 * kHeadDim) + 2 * c;
+    const uint4* qp = reinterpret_cast<const uint4*>(p.q + row0 * kHeadDim) + c;
 #pragma unroll
-    for (int h = 0; h < G; ++h) words(qp[h * 16], qp[h * 16 + 1], qw[h]);
+    for (int h = 0; h < G; ++h) words4(qp[h * (kHeadDim / 8)], qw[h]);
   }
   __syncthreads();
 
@@ -207,55 +240,55 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_partition_kernel(DecodePa
     st.m[h] = kEmptyMax;
     st.l[h] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st.acc[h][i] = 0.f;
+    for (int i = 0; i < 8; ++i) st.acc[h][i] = 0.f;
   }
 
   const size_t blk_stride = static_cast<size_t>(p.Hkv) * kTileElems;
   const uint16_t* kg = p.k_cache + static_cast<size_t>(g) * kTileElems;
   const uint16_t* vg = p.v_cache + static_cast<size_t>(g) * kTileElems;
-  const int lane_vec = grp * (kHeadDim / 8) + 2 * c;  // uint4 index of this lane's first K/V word
-  const int tail_blk = (L % kBlockSize) ? nblk - 1 : -1;
-  const int t0 = grp, t1 = grp + 8;
-  const int rem = L - (nblk - 1) * kBlockSize;  // tokens in the last block
 
-  Tile A, B;
-  int i = wave;
-  if (i < nb) {
-    const size_t o = static_cast<size_t>(uniform(s_bt[i])) * blk_stride;
-    load_tile(A, kg + o, vg + o, lane_vec);
+  // This wave's full tiles are local blocks wave, wave + 4, ... (n of them).
+  // A ring of kPrefetch + 1 register tiles keeps kPrefetch tiles in flight
+  // while one is consumed.  Every load is issued unconditionally (tiles past
+  // n are masked by their buffer range), so the compiler's vmcnt bookkeeping
+  // sees one straight-line schedule and waits only for the oldest tile.
+  const int n = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
+  auto issue = [&](Tile& dst, int t) {
+    const bool ok = t < n;
+    const size_t o = ok ? static_cast<size_t>(uniform(s_bt[wave + t * kWaves])) * blk_stride : 0;
+    const int bytes = ok ? kTileElems * 2 : 0;
+    load_tile(dst, tile_rsrc(kg + o, bytes), tile_rsrc(vg + o, bytes), lane);
+  };
+  Tile ring[kPrefetch + 1];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) issue(ring[k], k);
+  for (int t = 0; t < n; t += kPrefetch + 1) {
+#pragma unroll
+    for (int k = 0; k <= kPrefetch; ++k) {
+      issue(ring[(k + kPrefetch) % (kPrefetch + 1)], t + k + kPrefetch);
+      if (t + k < n) consume<G, false>(st, ring[k], qw, p.scale_log2, r, kBlockSize);
+    }
   }
-  for (; i < nb; i += 2 * kWaves) {
-    const int i2 = i + kWaves;
-    if (i2 < nb) {
-      const size_t o = static_cast<size_t>(uniform(s_bt[i2])) * blk_stride;
-      load_tile(B, kg + o, vg + o, lane_vec);
-    }
-    consume<G>(st, A, qw, p.scale_log2, blk0 + i == tail_blk, t0 < rem, t1 < rem);
-    if (i2 >= nb) break;
-    const int i3 = i2 + kWaves;
-    if (i3 < nb) {
-      const size_t o = static_cast<size_t>(uniform(s_bt[i3])) * blk_stride;
-      load_tile(A, kg + o, vg + o, lane_vec);
-    }
-    consume<G>(st, B, qw, p.scale_log2, blk0 + i2 == tail_blk, t0 < rem, t1 < rem);
+  if (has_tail && wave == (nb - 1) % kWaves) {
+    const size_t o = static_cast<size_t>(uniform(s_bt[nb - 1])) * blk_stride;
+    const int bytes = rem * kHeadDim * 2;
+    load_tile(ring[0], tile_rsrc(kg + o, bytes), tile_rsrc(vg + o, bytes), lane);
+    consume<G, true>(st, ring[0], qw, p.scale_log2, r, rem);
   }
 
-  // merge the 8 groups of this wave: lanes c, c+8, ..., c+56 hold the same dims
+  // merge the 4 rows of this wave: lanes c, c+16, c+32, c+48 hold the same dims
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float M = st.m[h];
-    M = fmaxf(M, dpp<kDppRowRor8>(M));
     M = fmaxf(M, __shfl_xor(M, 16));
     M = fmaxf(M, __shfl_xor(M, 32));
     const float f = fast_exp2(st.m[h] - M);
     float l = st.l[h] * f;
-    l += dpp<kDppRowRor8>(l);
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < 8; ++k) {
       float a = st.acc[h][k] * f;
-      a += dpp<kDppRowRor8>(a);
       a += __shfl_xor(a, 16);
       a += __shfl_xor(a, 32);
       st.acc[h][k] = a;
@@ -263,13 +296,12 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_partition_kernel(DecodePa
     st.m[h] = M;
     st.l[h] = l;
   }
-  if (grp == 0) {
+  if (r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float4* dst = reinterpret_cast<float4*>(&s_o[wave][h][16 * c]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        dst[k] = make_float4(st.acc[h][4 * k], st.acc[h][4 * k + 1], st.acc[h][4 * k + 2], st.acc[h][4 * k + 3]);
+      float4* dst = reinterpret_cast<float4*>(&s_o[wave][h][8 * c]);
+      dst[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
+      dst[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
     }
     if (c == 0) {
 #pragma unroll

@@ -43,6 +43,7 @@ enum : int {
   kDppQuadXor2 = 0x4E,       // quad_perm [2,3,0,1]
   kDppRowHalfMirror = 0x141, // lane i <-> 7 - i within each half-row
   kDppRowRor8 = 0x128,       // lane i <- (i + 8) mod 16 within each row
+  kDppRowMirror = 0x140,     // lane i <-> 15 - i within each row
 };
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
