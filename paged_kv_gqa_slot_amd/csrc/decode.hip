@@ -40,8 +40,17 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr float kEmptyMax = -1.0e30f;   // running max before the first valid token
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int kTargetWorkgroups = 2048;  // automatic split-K aims for this many pass-1 workgroups
-constexpr int kMinPartBlocks = 8;        // ... but no partition shorter than 128 tokens
+// Automatic split-K (measured on MI355X, 256 CUs):
+//  * at least kAutoMinParts partitions of the longest context, which keeps
+//    ragged batches balanced (partitions of ~1K tokens at 8K contexts);
+//  * at least kAutoFillWgs pass-1 workgroups (two per CU), rounded up to a
+//    whole number of CU rounds when the grid is small, since uniform
+//    contexts run best when every CU gets the same number of workgroups;
+//  * no partition shorter than kAutoMinPartBlocks blocks (256 tokens).
+constexpr int kCuCount = 256;
+constexpr int kAutoMinParts = 8;
+constexpr int kAutoFillWgs = 2 * kCuCount;
+constexpr int kAutoMinPartBlocks = 16;
 #ifndef FE_DECODE_PREFETCH
 #define FE_DECODE_PREFETCH 1
 #endif
@@ -394,10 +403,15 @@ bool plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_partitions
       P = num_partitions;
     } else {
       const long pairs = static_cast<long>(B) * Hkv;
-      P = static_cast<int>((kTargetWorkgroups + pairs - 1) / pairs);
-      const int pmax = (nblk_max + kMinPartBlocks - 1) / kMinPartBlocks;
-      if (P > pmax) P = pmax;
-      if (P < 1) P = 1;
+      long pa = (kAutoFillWgs + pairs - 1) / pairs;
+      if (pa < kAutoMinParts) pa = kAutoMinParts;
+      if (pairs * pa <= 8L * kCuCount) {  // small grid: whole CU rounds
+        const long wgs = (pairs * pa + kCuCount - 1) / kCuCount * kCuCount;
+        pa = (wgs + pairs - 1) / pairs;
+      }
+      const long pmax = (nblk_max + kAutoMinPartBlocks - 1) / kAutoMinPartBlocks;
+      if (pa > pmax) pa = pmax;
+      P = static_cast<int>(pa < 1 ? 1 : pa);
     }
     if (P > nblk_max) P = nblk_max;
     int part_blocks = (nblk_max + P - 1) / P;

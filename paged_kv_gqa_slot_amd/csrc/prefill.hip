@@ -1,7 +1,343 @@
-// Chunked prefill (MFMA) -- placeholder until the kernel lands.
+// Chunked prefill over the paged cache on the bf16 MFMA units (ForgeEngine
+// README, "What it implements": restricted prefill lab, and "Scheduling":
+// token-budgeted batching that cuts prompts into chunks; "Make the Engine
+// Talk" section 1.2: the prefill pass that primes the cache).
+//
+// A chunk of C queries sits at the end of its sequence: query i is at
+// position L - C + i and attends to keys 0 .. L - C + i.
+//
+// One workgroup per (sequence, KV head, tile of QT query rows).  Its W waves
+// each own 32 (query row, query head) pairs of the group -- one head per wave
+// when G >= 4 -- so every K/V tile staged in LDS is shared by all G heads.
+// Per 64-key tile each wave computes
+//   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
+//                      B = Q^T held in registers (32 queries x 128 dims)
+//   online softmax     the D layout puts query (lane % 32) in every lane, so
+//                      the row max/sum are lane-local plus one permlane32 swap
+//   O^T += V^T P^T     B = P^T packed to bf16 straight from the S^T registers;
+//                      A = V^T read from the row-major V tile with
+//                      ds_read_b64_tr_b16 (two 4-key transposed reads).
+// The MFMA sums over keys in any order as long as A and B agree, so the
+// k-slot -> key order of each PV step is chosen to match the keys the S^T
+// accumulator layout leaves in each lane (no data movement for P).
+// LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled by a function of
+// the key so that both the K row reads and the transposed V reads are free
+// of bank conflicts.  K/V tiles are double-buffered: the next tile's global
+// loads are issued before the current tile's math.
+#include <math.h>
+
 #include "fe_device.h"
 #include "fe_kernels.h"
 
 namespace fe {
-hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kKeysPerTile = 64;
+constexpr int kRowBytes = kHeadDim * 2;                    // 256
+constexpr int kTileBytes = kKeysPerTile * kRowBytes;       // 16 KiB
+constexpr int kChunksPerTile = kTileBytes / 16;            // 1024
+constexpr float kRescaleSlack = 8.0f;
+constexpr float kEmptyMax = -1.0e30f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct PrefillParams {
+  const uint16_t* q;
+  const int32_t* query_start_loc;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  uint16_t* out;
+  float* lse;
+  int max_blocks, B, total_q, max_q_len, Hq, Hkv, num_blocks, ctx_cap, qtiles;
+  float scale_log2;
+};
+
+template <int G>
+struct Shape {
+  static constexpr int W = (G <= 4 && 4 % G == 0) ? 4 : G;  // waves per workgroup
+  static constexpr int QT = 32 * W / G;                     // query rows per workgroup
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kChunksPerThread = (kChunksPerTile + kThreads - 1) / kThreads;
+};
+
+// Swizzle of the 16-byte chunk index inside a 256-byte LDS row.
+__device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+__device__ __forceinline__ int lds_off(int key, int chunk) { return key * kRowBytes + ((chunk ^ swz(key)) << 4); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int G>
+__global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(PrefillParams p) {
+  using S = Shape<G>;
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[2][kTileBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int col = lane & 31;   // this lane's query within the wave's 32
+  const int half = lane >> 5;  // which 8-dim / 4-key half of an MFMA operand
+
+  int wg = blockIdx.x;
+  const int qt = wg % p.qtiles;
+  wg /= p.qtiles;
+  const int g = wg % p.Hkv;
+  const int b = wg / p.Hkv;
+
+  const int q0 = p.query_start_loc[b];
+  int C = p.query_start_loc[b + 1] - q0;
+  C = C < 0 ? 0 : (C > p.max_q_len ? p.max_q_len : C);
+  const int i0 = qt * S::QT;
+  if (i0 >= C) return;
+  int L = p.context_lens[b];
+  L = L < 0 ? 0 : (L > p.ctx_cap ? p.ctx_cap : L);
+
+  // this wave's (head, query) rows: head h_loc, queries i0 + qoff .. + 31
+  const int h_loc = (wave * 32) / S::QT;
+  const int qoff = (wave * 32) % S::QT;
+  const int qi = i0 + qoff + col;              // this lane's query index in the chunk
+  const bool q_valid = qi < C && q0 + qi < p.total_q;
+  const int pos = L - C + qi;                  // its position; keys 0..pos are visible
+  const int head = g * G + h_loc;
+
+  // Q^T operand: k-step kk covers dims 16 kk .. 16 kk + 15; this lane holds 8.
+  bf16x8_t qb[8];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(p.q + (static_cast<size_t>(q0 + qi) * p.Hq + head) * kHeadDim);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qb[kk] = as_bf16x8(q_valid ? qp[2 * kk + half] : make_uint4(0, 0, 0, 0));
+  }
+
+  // keys this workgroup needs: 0 .. last visible position of its last query
+  const int last_q = min(i0 + S::QT, C) - 1;
+  const int kv_end = max(0, min(L, L - C + last_q + 1));
+  const int n_tiles = (kv_end + kKeysPerTile - 1) / kKeysPerTile;
+  const int diag_from = max(0, L - C + i0 + 1);  // keys beyond this need the causal mask for some row
+
+  const int32_t* bt = p.block_tables + static_cast<size_t>(b) * p.max_blocks;
+  const size_t blk_stride = static_cast<size_t>(p.Hkv) * kTileElems;
+  const uint16_t* kg = p.k_cache + static_cast<size_t>(g) * kTileElems;
+  const uint16_t* vg = p.v_cache + static_cast<size_t>(g) * kTileElems;
+
+  // staging: thread copies chunks tid + k * kThreads of each tile
+  uint4 rk[S::kChunksPerThread], rv[S::kChunksPerThread];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int k = 0; k < S::kChunksPerThread; ++k) {
+      const int c = tid + k * S::kThreads;
+      const int key = t * kKeysPerTile + c / 16;
+      if (c >= kChunksPerTile) break;
+      if (key < L) {
+        const int blk = min(max(bt[key / kBlockSize], 0), p.num_blocks - 1);
+        const size_t off = static_cast<size_t>(blk) * blk_stride + (key % kBlockSize) * kHeadDim + (c % 16) * 8;
+        rk[k] = *reinterpret_cast<const uint4*>(kg + off);
+        rv[k] = *reinterpret_cast<const uint4*>(vg + off);
+      } else {  // past the context: zeros (never NaN) so masked keys stay inert
+        rk[k] = make_uint4(0, 0, 0, 0);
+        rv[k] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < S::kChunksPerThread; ++k) {
+      const int c = tid + k * S::kThreads;
+      if (c >= kChunksPerTile) break;
+      const int o = lds_off(c / 16, c % 16);
+      *reinterpret_cast<uint4*>(&s_k[buf][o]) = rk[k];
+      *reinterpret_cast<uint4*>(&s_v[buf][o]) = rv[k];
+    }
+  };
+
+  f32x16_t o_acc[4];  // O^T, dim block d: lane holds query col, dims 32 d + 8 (i / 4) + 4 half + i % 4
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o_acc[d][i] = 0.f;
+  float m = kEmptyMax, lsum = 0.f;
+
+  if (n_tiles > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) fetch(t + 1);
+
+    // S^T for keys 64 t + 32 blk + (0..31)
+    f32x16_t s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x16_t acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      const int key = 32 * blk + col;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[buf][lds_off(key, 2 * kk + half)]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qb[kk], acc, 0, 0, 0);
+      }
+      s[blk] = acc;
+    }
+
+    // scale, causal mask, running max (log2 domain)
+    const bool diag = t * kKeysPerTile + kKeysPerTile > diag_from;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = s[blk][i] * p.scale_log2;
+        if (diag) {
+          const int key = t * kKeysPerTile + 32 * blk + 8 * (i / 4) + 4 * half + (i % 4);
+          if (key > pos || !q_valid) v = -INFINITY;
+        }
+        s[blk][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    if (__any(mx > m + kRescaleSlack)) {
+      if (mx > m + kRescaleSlack) {
+        const float a = fast_exp2(m - mx);
+        m = mx;
+        lsum *= a;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o_acc[d][i] *= a;
+      }
+    }
+
+    // P^T (bf16) for k-step (blk, tau): this lane's S^T entries 8 tau .. 8 tau + 7
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        uint4 w;
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          e[j] = fast_exp2(s[blk][8 * tau + j] - m);
+          lsum += e[j];
+        }
+        w.x = pack_bf16x2(e[0], e[1]);
+        w.y = pack_bf16x2(e[2], e[3]);
+        w.z = pack_bf16x2(e[4], e[5]);
+        w.w = pack_bf16x2(e[6], e[7]);
+        pb[blk][tau] = as_bf16x8(w);
+      }
+
+    // O^T += V^T P^T.  k-slots of step (blk, tau): slots 0-3 / 4-7 / 8-11 / 12-15
+    // are keys 32 blk + 16 tau + {0-3, 8-11, 4-7, 12-15}.  Lanes of 16-lane
+    // group gq hold k-slots 8 (gq / 2) .. + 7 of dims 16 (gq % 2) .. + 15.
+    const int gq = lane >> 4;
+    const int src = lane & 15;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const int key_a = 32 * blk + 16 * tau + 4 * (gq >> 1) + (src >> 2);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int chunk = 4 * d + 2 * (gq & 1) + ((src & 3) >> 1);
+          const int inner = 8 * (src & 1);
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(&s_v[buf][lds_off(key_a, chunk) + inner]));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(&s_v[buf][lds_off(key_a + 8, chunk) + inner]));
+          // move whole dwords: element-wise 16-bit extraction here is lowered
+          // into half-word shuffles that drop the upper dword of each read
+          const uint2 l2 = __builtin_bit_cast(uint2, lo);
+          const uint2 h2 = __builtin_bit_cast(uint2, hi);
+          const bf16x8_t va = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+          o_acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][tau], o_acc[d], 0, 0, 0);
+        }
+      }
+
+    // buffer buf ^ 1 was last read in the previous iteration, which every wave
+    // finished before that iteration's barrier
+    if (t + 1 < n_tiles) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // combine the two lane halves of each query's sum, normalise, write
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (!q_valid) return;
+  const bool empty = !(lsum > 0.f);
+  const float inv = empty ? 0.f : 1.f / lsum;
+  const size_t row = static_cast<size_t>(q0 + qi) * p.Hq + head;
+  uint16_t* orow = p.out + row * kHeadDim;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dim = 32 * d + 8 * r4 + 4 * half;
+      uint2 w;
+      w.x = pack_bf16x2(o_acc[d][4 * r4] * inv, o_acc[d][4 * r4 + 1] * inv);
+      w.y = pack_bf16x2(o_acc[d][4 * r4 + 2] * inv, o_acc[d][4 * r4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + dim) = w;
+    }
+  if (half == 0 && p.lse) p.lse[row] = empty ? -INFINITY : (m + log2f(lsum)) * kLn2;
+}
+
+template <int G>
+hipError_t launch_g(const PrefillParams& prm, hipStream_t stream) {
+  PrefillParams copy = prm;
+  copy.qtiles = (prm.max_q_len + Shape<G>::QT - 1) / Shape<G>::QT;
+  const long grid = static_cast<long>(copy.qtiles) * prm.Hkv * prm.B;
+  if (grid == 0) return hipSuccess;
+  void* args[] = {&copy};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gqa_prefill_chunk_kernel<G>), dim3(static_cast<unsigned>(grid)),
+                         dim3(Shape<G>::kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  PrefillParams prm{};
+  prm.q = static_cast<const uint16_t*>(a.q);
+  prm.query_start_loc = a.query_start_loc;
+  prm.k_cache = static_cast<const uint16_t*>(a.k_cache);
+  prm.v_cache = static_cast<const uint16_t*>(a.v_cache);
+  prm.block_tables = a.block_tables;
+  prm.context_lens = a.context_lens;
+  prm.out = static_cast<uint16_t*>(a.out);
+  prm.lse = a.lse;
+  prm.max_blocks = a.max_blocks_per_seq;
+  prm.B = a.B;
+  prm.total_q = a.total_q;
+  prm.max_q_len = a.max_q_len;
+  prm.Hq = a.Hq;
+  prm.Hkv = a.Hkv;
+  prm.num_blocks = a.num_blocks;
+  const long cap_bt = static_cast<long>(a.max_blocks_per_seq) * kBlockSize;
+  prm.ctx_cap = static_cast<int>(a.max_context_len < cap_bt ? a.max_context_len : cap_bt);
+  prm.scale_log2 = a.scale * kLog2e;
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_g<1>(prm, stream);
+    case 2: return launch_g<2>(prm, stream);
+    case 3: return launch_g<3>(prm, stream);
+    case 4: return launch_g<4>(prm, stream);
+    case 5: return launch_g<5>(prm, stream);
+    case 6: return launch_g<6>(prm, stream);
+    case 7: return launch_g<7>(prm, stream);
+    case 8: return launch_g<8>(prm, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace fe
