@@ -12,6 +12,7 @@ in GB/s; `roofline` is for the decode call, timed with HIP events on the
 stream its kernels run on; `cpu_baseline` is the fp64 oracle on the host.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -54,6 +55,40 @@ def prefill_flops(w) -> int:
     return tot * w.Hq * 4 * 128
 
 
+def kernel_source_digest(kind: str) -> str:
+    """Digest of the source file of the timed kernel (traffic counters are
+    only reported while they were taken on this exact source)."""
+    name = "decode.hip" if kind == "decode" else "prefill.hip"
+    with open(os.path.join(ROOT, "paged_kv_gqa_slot_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kind: str, num_partitions: int):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+    recorded in profiles/traffic.json (scaled by a plain copy of known size);
+    None when absent or taken on a different kernel source or partitioning."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != kernel_source_digest(kind):
+        return None
+    if kind == "decode" and rec.get("num_partitions") != num_partitions:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def prefill_row_flops(w, r: int) -> int:
+    qsl = w.query_start_loc.tolist()
+    for b, L in enumerate(w.context_lens.tolist()):
+        if qsl[b] <= r < qsl[b + 1]:
+            C = qsl[b + 1] - qsl[b]
+            return (L - C + (r - qsl[b]) + 1) * w.Hq * 4 * 128
+    return 0
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the fp64 oracle (as it stands) on the host cores."""
     import oracle
@@ -74,17 +109,25 @@ def cpu_baseline(w, budget_s: float):
                 "sample": f"fp64 oracle decode over the full workload ({w.kv_tokens} KV tokens x {w.Hkv} KV heads), "
                           f"{reps} repetitions, {per * 1e3:.1f} ms each; append not included",
                 "kv_tokens_per_s": round(w.kv_tokens / per, 1)}
-    # prefill: a bounded sample of packed rows, scaled to the whole chunk
+    # prefill: a bounded, evenly spread sample of packed rows, scaled to the
+    # whole chunk (a probe of 32 rows sizes the sample to the time budget)
     total_q = lay.q.shape[0]
-    n = max(1, min(total_q, 64))
-    rows = list(range(0, total_q, max(1, total_q // n)))[:n]
-    t0 = time.perf_counter()
-    oracle.prefill_chunk(lay.q, w.query_start_loc, rk, rv, w.block_tables, w.context_lens, w.scale, rows=rows,
-                         nthreads=threads)
-    el = time.perf_counter() - t0
-    frac = len(rows) / total_q
-    return {"value": round(prefill_flops(w) * frac / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "sample": f"fp64 oracle prefill on {len(rows)} of {total_q} query rows ({el:.1f} s)"}
+
+    def run(n):
+        rows = [int(round(i * (total_q - 1) / max(1, n - 1))) for i in range(n)] if n > 1 else [0]
+        t0 = time.perf_counter()
+        oracle.prefill_chunk(lay.q, w.query_start_loc, rk, rv, w.block_tables, w.context_lens, w.scale, rows=rows,
+                             nthreads=threads)
+        return rows, time.perf_counter() - t0
+
+    rows, el = run(min(total_q, 32))
+    n = int(min(total_q, max(len(rows), len(rows) * budget_s / max(el, 1e-3))))
+    if n > len(rows):
+        rows, el = run(n)
+    flops = sum(prefill_row_flops(w, r) for r in rows)
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle prefill on {len(rows)} of {total_q} query rows spread over the chunk "
+                      f"({el:.1f} s); flops counted for those rows"}
 
 
 def main():
@@ -97,6 +140,8 @@ def main():
     ap.add_argument("--partitions", type=int, default=0, help="decode split-K factor (0 = automatic)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run 3 plain device copies of this many MiB (rocprofv3 counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -185,7 +230,8 @@ def main():
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
         achieved = att_bytes / (att_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(spec.name, "decode", P),
                 "kernel": "fe_paged_gqa_decode (gqa_decode_partition_kernel + gqa_decode_merge_kernel)"
                           if P > 1 else "fe_paged_gqa_decode (gqa_decode_partition_kernel)",
                 "per_launch_bytes": att_bytes, "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5)}
@@ -199,12 +245,23 @@ def main():
         value = nl * flops / (ms_per_step * 1e-3) / 1e12
         achieved = flops / (att_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                "traffic": measured_traffic(spec.name, "prefill", 0),
                 "kernel": "fe_paged_gqa_prefill_chunk (gqa_prefill_chunk_kernel)", "per_launch_flops": flops,
                 "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5)}
         metric = "paged GQA chunked-prefill TFLOP/s (% of bf16 MFMA peak), Qwen3-4B shape"
         unit = "TFLOP/s"
         extra = {}
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"ran 3 device copies of {args.calibrate_copy_mib} MiB for counter calibration")
 
     cpu = None
     if not args.no_cpu_baseline:
