@@ -83,11 +83,14 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
   const int col = lane & 31;   // this lane's query within the wave's 32
   const int half = lane >> 5;  // which 8-dim / 4-key half of an MFMA operand
 
-  int wg = blockIdx.x;
-  const int qt = wg % p.qtiles;
-  wg /= p.qtiles;
-  const int g = wg % p.Hkv;
-  const int b = wg / p.Hkv;
+  // Workgroups are dispatched round-robin over the 8 XCDs (id mod 8).  The
+  // query tile is the slowest-varying index, so all tiles of one (sequence,
+  // KV head) pair share an XCD and read its K/V through one L2.
+  const int pairs = p.B * p.Hkv;
+  const int qt = blockIdx.x / pairs;
+  const int pair = blockIdx.x % pairs;
+  const int g = pair % p.Hkv;
+  const int b = pair / p.Hkv;
 
   const int q0 = p.query_start_loc[b];
   int C = p.query_start_loc[b + 1] - q0;
