@@ -26,6 +26,8 @@
 // loads are issued before the current tile's math.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fe_device.h"
 #include "fe_kernels.h"
 
@@ -62,7 +64,8 @@ struct Shape {
   static constexpr int W = (G <= 4 && 4 % G == 0) ? 4 : G;  // waves per workgroup
   static constexpr int QT = 32 * W / G;                     // query rows per workgroup
   static constexpr int kThreads = 64 * W;
-  static constexpr int kChunksPerThread = (kChunksPerTile + kThreads - 1) / kThreads;
+  // a 64-key tile is 4 KV blocks; wave w stages blocks w, w + W, ... of it
+  static constexpr int kStageBlocks = (4 + W - 1) / W;
 };
 
 // Swizzle of the 16-byte chunk index inside a 256-byte LDS row.
@@ -127,35 +130,80 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
   const uint16_t* kg = p.k_cache + static_cast<size_t>(g) * kTileElems;
   const uint16_t* vg = p.v_cache + static_cast<size_t>(g) * kTileElems;
 
-  // staging: thread copies chunks tid + k * kThreads of each tile
-  uint4 rk[S::kChunksPerThread], rv[S::kChunksPerThread];
+  // Staging: wave w copies blocks w, w + W, ... of each 64-key tile, each a
+  // contiguous 4 KiB (block, KV head) run, lane reading 16 bytes at
+  // lane + 64 j.  Rows past the context come back as zeros from the buffer
+  // range (never NaN, so masked keys stay inert in the PV product).
+  const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
+  int st_off[4];  // LDS byte offset (within a block's 4 KiB) of this lane's 4 staged chunks
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st_off[j] = lds_off(4 * j + (lane >> 4), lane & 15);
+  uint4 rk[S::kStageBlocks][4], rv[S::kStageBlocks][4];
   auto fetch = [&](int t) {
 #pragma unroll
-    for (int k = 0; k < S::kChunksPerThread; ++k) {
-      const int c = tid + k * S::kThreads;
-      const int key = t * kKeysPerTile + c / 16;
-      if (c >= kChunksPerTile) break;
-      if (key < L) {
-        const int blk = min(max(bt[key / kBlockSize], 0), p.num_blocks - 1);
-        const size_t off = static_cast<size_t>(blk) * blk_stride + (key % kBlockSize) * kHeadDim + (c % 16) * 8;
-        rk[k] = *reinterpret_cast<const uint4*>(kg + off);
-        rv[k] = *reinterpret_cast<const uint4*>(vg + off);
-      } else {  // past the context: zeros (never NaN) so masked keys stay inert
-        rk[k] = make_uint4(0, 0, 0, 0);
-        rv[k] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < S::kStageBlocks; ++i) {
+      const int bl = wave + i * S::W;
+      if (bl < 4) {
+        const int gb = 4 * t + bl;  // block index within the sequence
+        const bool ok = gb < nblk_seq;
+        const int blk = ok ? min(max(bt[gb], 0), p.num_blocks - 1) : 0;
+        const int rows = ok ? min(kBlockSize, L - gb * kBlockSize) : 0;
+        const size_t o = static_cast<size_t>(blk) * blk_stride;
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(kg + o), static_cast<short>(0), rows * kRowBytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(vg + o), static_cast<short>(0), rows * kRowBytes, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kr, lane * 16 + 1024 * j, 0, 0);
+          const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(vr, lane * 16 + 1024 * j, 0, 0);
+          rk[i][j] = make_uint4(a[0], a[1], a[2], a[3]);
+          rv[i][j] = make_uint4(c[0], c[1], c[2], c[3]);
+        }
       }
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int k = 0; k < S::kChunksPerThread; ++k) {
-      const int c = tid + k * S::kThreads;
-      if (c >= kChunksPerTile) break;
-      const int o = lds_off(c / 16, c % 16);
-      *reinterpret_cast<uint4*>(&s_k[buf][o]) = rk[k];
-      *reinterpret_cast<uint4*>(&s_v[buf][o]) = rv[k];
+    for (int i = 0; i < S::kStageBlocks; ++i) {
+      const int bl = wave + i * S::W;
+      if (bl < 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          *reinterpret_cast<uint4*>(&s_k[buf][bl * 4096 + st_off[j]]) = rk[i][j];
+          *reinterpret_cast<uint4*>(&s_v[buf][bl * 4096 + st_off[j]]) = rv[i][j];
+        }
+      }
     }
   };
+
+  // per-lane LDS read offsets (the same for both buffers)
+  int k_off[2][8];  // K row reads for S^T: key 32 blk + col, dims 16 kk + 8 half
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) k_off[blk][kk] = lds_off(32 * blk + col, 2 * kk + half);
+  // transposed V reads: k-slots of step (blk, tau) are keys 32 blk + 16 tau +
+  // {0-3, 8-11, 4-7, 12-15}; 16-lane group gq holds slots 8 (gq / 2) .. + 7 of
+  // dims 16 (gq % 2) .. + 15 of each 32-dim block d
+  int v_off[2][2][4][2];
+  {
+    const int gq = lane >> 4;
+    const int src = lane & 15;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const int key_a = 32 * blk + 16 * tau + 4 * (gq >> 1) + (src >> 2);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int chunk = 4 * d + 2 * (gq & 1) + ((src & 3) >> 1);
+          const int inner = 8 * (src & 1);
+          v_off[blk][tau][d][0] = lds_off(key_a, chunk) + inner;
+          v_off[blk][tau][d][1] = lds_off(key_a + 8, chunk) + inner;
+        }
+      }
+  }
 
   f32x16_t o_acc[4];  // O^T, dim block d: lane holds query col, dims 32 d + 8 (i / 4) + 4 half + i % 4
 #pragma unroll
@@ -170,8 +218,14 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
   }
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  // one 64-key tile on LDS buffer `buf` (a compile-time constant, so the
+  // buffer offset folds into the LDS instruction immediates)
+  // bufc / diagc are std::integral_constant in the main loop (the buffer
+  // offset then folds into the LDS instruction immediates) and plain values
+  // for the few diagonal tiles at the end.
+  auto tile_step = [&](auto bufc, auto diagc, int t) {
+    const int buf = static_cast<int>(bufc);
+    const bool diag = static_cast<bool>(diagc);  // tile reaches past some row's position
     if (t + 1 < n_tiles) fetch(t + 1);
 
     // S^T for keys 64 t + 32 blk + (0..31)
@@ -181,17 +235,15 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
       f32x16_t acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      const int key = 32 * blk + col;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[buf][lds_off(key, 2 * kk + half)]);
+        const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[buf][k_off[blk][kk]]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qb[kk], acc, 0, 0, 0);
       }
       s[blk] = acc;
     }
 
     // scale, causal mask, running max (log2 domain)
-    const bool diag = t * kKeysPerTile + kKeysPerTile > diag_from;
     float mx = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -241,24 +293,17 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
         pb[blk][tau] = as_bf16x8(w);
       }
 
-    // O^T += V^T P^T.  k-slots of step (blk, tau): slots 0-3 / 4-7 / 8-11 / 12-15
-    // are keys 32 blk + 16 tau + {0-3, 8-11, 4-7, 12-15}.  Lanes of 16-lane
-    // group gq hold k-slots 8 (gq / 2) .. + 7 of dims 16 (gq % 2) .. + 15.
-    const int gq = lane >> 4;
-    const int src = lane & 15;
+    // O^T += V^T P^T
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        const int key_a = 32 * blk + 16 * tau + 4 * (gq >> 1) + (src >> 2);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const int chunk = 4 * d + 2 * (gq & 1) + ((src & 3) >> 1);
-          const int inner = 8 * (src & 1);
           const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(&s_v[buf][lds_off(key_a, chunk) + inner]));
+              (__attribute__((address_space(3))) s16x4_t*)(&s_v[buf][v_off[blk][tau][d][0]]));
           const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(&s_v[buf][lds_off(key_a + 8, chunk) + inner]));
+              (__attribute__((address_space(3))) s16x4_t*)(&s_v[buf][v_off[blk][tau][d][1]]));
           // move whole dwords: element-wise 16-bit extraction here is lowered
           // into half-word shuffles that drop the upper dword of each read
           const uint2 l2 = __builtin_bit_cast(uint2, lo);
@@ -272,7 +317,18 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
     // finished before that iteration's barrier
     if (t + 1 < n_tiles) stash(buf ^ 1);
     __syncthreads();
+  };
+  // tiles below n_plain end at or before every row's position and need no mask
+  const int n_plain = min(n_tiles, diag_from / kKeysPerTile);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using Plain = std::false_type;
+  int t = 0;
+  for (; t + 1 < n_plain; t += 2) {
+    tile_step(B0{}, Plain{}, t);
+    tile_step(B1{}, Plain{}, t + 1);
   }
+  for (; t < n_tiles; ++t) tile_step(t & 1, t >= n_plain, t);
 
   // combine the two lane halves of each query's sum, normalise, write
   {
