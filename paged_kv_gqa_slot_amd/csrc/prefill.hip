@@ -6,9 +6,12 @@
 // A chunk of C queries sits at the end of its sequence: query i is at
 // position L - C + i and attends to keys 0 .. L - C + i.
 //
-// One workgroup per (sequence, KV head, tile of QT query rows).  Its W waves
+// One workgroup per (sequence, KV head, tile of QT query rows).  W waves
 // each own 32 (query row, query head) pairs of the group -- one head per wave
 // when G >= 4 -- so every K/V tile staged in LDS is shared by all G heads.
+// When W <= 4 the workgroup has KS = 2 such wave groups that split the key
+// range in two halves (two waves per SIMD instead of one) and merge their
+// (max, sum, O) by log-sum-exp through LDS at the end.
 // Per 64-key tile each wave computes
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
 //                      B = Q^T held in registers (32 queries x 128 dims)
@@ -20,10 +23,11 @@
 // The MFMA sums over keys in any order as long as A and B agree, so the
 // k-slot -> key order of each PV step is chosen to match the keys the S^T
 // accumulator layout leaves in each lane (no data movement for P).
-// LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled by a function of
-// the key so that both the K row reads and the transposed V reads are free
-// of bank conflicts.  K/V tiles are double-buffered: the next tile's global
-// loads are issued before the current tile's math.
+// LDS rows are padded (K: 272 bytes, V: 288 bytes) so that the K row reads of
+// 16 consecutive keys and the 4-key transposed V reads are free of bank
+// conflicts, and every LDS offset is a per-lane base plus a constant.  Each
+// group's K/V tiles are double-buffered: the next tile's global loads are
+// issued before the current tile's math.
 #include <math.h>
 
 #include <type_traits>
@@ -35,9 +39,12 @@ namespace fe {
 namespace {
 
 constexpr int kKeysPerTile = 64;
-constexpr int kRowBytes = kHeadDim * 2;                    // 256
-constexpr int kTileBytes = kKeysPerTile * kRowBytes;       // 16 KiB
-constexpr int kChunksPerTile = kTileBytes / 16;            // 1024
+constexpr int kRowBytes = kHeadDim * 2;                 // 256 bytes of one K/V row
+constexpr int kKStride = kRowBytes + 16;                // padded LDS row strides
+constexpr int kVStride = kRowBytes + 32;
+constexpr int kKTileBytes = kKeysPerTile * kKStride;    // 17408
+constexpr int kVTileBytes = kKeysPerTile * kVStride;    // 18432
+constexpr int kBufBytes = kKTileBytes + kVTileBytes;    // one K + V tile
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kEmptyMax = -1.0e30f;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -61,28 +68,27 @@ struct PrefillParams {
 
 template <int G>
 struct Shape {
-  static constexpr int W = (G <= 4 && 4 % G == 0) ? 4 : G;  // waves per workgroup
+  static constexpr int W = (G <= 4 && 4 % G == 0) ? 4 : G;  // waves per group
+  static constexpr int KS = W <= 4 ? 2 : 1;                 // groups splitting the keys
   static constexpr int QT = 32 * W / G;                     // query rows per workgroup
-  static constexpr int kThreads = 64 * W;
-  // a 64-key tile is 4 KV blocks; wave w stages blocks w, w + W, ... of it
+  static constexpr int kThreads = 64 * W * KS;
+  // a 64-key tile is 4 KV blocks; wave w of a group stages blocks w, w + W, ...
   static constexpr int kStageBlocks = (4 + W - 1) / W;
+  static constexpr int kLdsBytes = 2 * KS * kBufBytes;
 };
-
-// Swizzle of the 16-byte chunk index inside a 256-byte LDS row.
-__device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
-__device__ __forceinline__ int lds_off(int key, int chunk) { return key * kRowBytes + ((chunk ^ swz(key)) << 4); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 template <int G>
 __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(PrefillParams p) {
   using S = Shape<G>;
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[S::kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
+  const int wave_all = uniform(tid >> 6);
+  const int grp = wave_all / S::W;  // which half of the key range
+  const int wave = wave_all % S::W;
   const int col = lane & 31;   // this lane's query within the wave's 32
   const int half = lane >> 5;  // which 8-dim / 4-key half of an MFMA operand
 
@@ -124,20 +130,26 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
   const int kv_end = max(0, min(L, L - C + last_q + 1));
   const int n_tiles = (kv_end + kKeysPerTile - 1) / kKeysPerTile;
   const int diag_from = max(0, L - C + i0 + 1);  // keys beyond this need the causal mask for some row
+  const int n_plain = min(n_tiles, diag_from / kKeysPerTile);  // tiles needing no mask
+  // group 0 takes tiles [0, nA), group 1 tiles [nA, n_tiles)
+  const int nA = S::KS == 2 ? (n_tiles + 1) / 2 : n_tiles;
+  const int t_first = grp * nA;
+  const int t_end = grp == 0 ? nA : n_tiles;
 
   const int32_t* bt = p.block_tables + static_cast<size_t>(b) * p.max_blocks;
   const size_t blk_stride = static_cast<size_t>(p.Hkv) * kTileElems;
   const uint16_t* kg = p.k_cache + static_cast<size_t>(g) * kTileElems;
   const uint16_t* vg = p.v_cache + static_cast<size_t>(g) * kTileElems;
+  const int grp_base = grp * 2 * kBufBytes;
 
   // Staging: wave w copies blocks w, w + W, ... of each 64-key tile, each a
   // contiguous 4 KiB (block, KV head) run, lane reading 16 bytes at
-  // lane + 64 j.  Rows past the context come back as zeros from the buffer
-  // range (never NaN, so masked keys stay inert in the PV product).
+  // lane + 64 j (token row 4 j + lane / 16, chunk lane % 16).  Rows past the
+  // context come back as zeros from the buffer range (never NaN, so masked
+  // keys stay inert in the PV product).
   const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
-  int st_off[4];  // LDS byte offset (within a block's 4 KiB) of this lane's 4 staged chunks
-#pragma unroll
-  for (int j = 0; j < 4; ++j) st_off[j] = lds_off(4 * j + (lane >> 4), lane & 15);
+  const int st_k = grp_base + (lane >> 4) * kKStride + (lane & 15) * 16;
+  const int st_v = grp_base + kKTileBytes + (lane >> 4) * kVStride + (lane & 15) * 16;
   uint4 rk[S::kStageBlocks][4], rv[S::kStageBlocks][4];
   auto fetch = [&](int t) {
 #pragma unroll
@@ -170,40 +182,23 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
       if (bl < 4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          *reinterpret_cast<uint4*>(&s_k[buf][bl * 4096 + st_off[j]]) = rk[i][j];
-          *reinterpret_cast<uint4*>(&s_v[buf][bl * 4096 + st_off[j]]) = rv[i][j];
+          const int row = 16 * bl + 4 * j;
+          *reinterpret_cast<uint4*>(&lds[st_k + buf * kBufBytes + row * kKStride]) = rk[i][j];
+          *reinterpret_cast<uint4*>(&lds[st_v + buf * kBufBytes + row * kVStride]) = rv[i][j];
         }
       }
     }
   };
 
-  // per-lane LDS read offsets (the same for both buffers)
-  int k_off[2][8];  // K row reads for S^T: key 32 blk + col, dims 16 kk + 8 half
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) k_off[blk][kk] = lds_off(32 * blk + col, 2 * kk + half);
+  // per-lane LDS read bases; everything else is a compile-time offset
+  // K rows for S^T: key 32 blk + col, dims 16 kk + 8 half
+  const int k_rd = grp_base + col * kKStride + half * 16;
   // transposed V reads: k-slots of step (blk, tau) are keys 32 blk + 16 tau +
   // {0-3, 8-11, 4-7, 12-15}; 16-lane group gq holds slots 8 (gq / 2) .. + 7 of
-  // dims 16 (gq % 2) .. + 15 of each 32-dim block d
-  int v_off[2][2][4][2];
-  {
-    const int gq = lane >> 4;
-    const int src = lane & 15;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const int key_a = 32 * blk + 16 * tau + 4 * (gq >> 1) + (src >> 2);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int chunk = 4 * d + 2 * (gq & 1) + ((src & 3) >> 1);
-          const int inner = 8 * (src & 1);
-          v_off[blk][tau][d][0] = lds_off(key_a, chunk) + inner;
-          v_off[blk][tau][d][1] = lds_off(key_a + 8, chunk) + inner;
-        }
-      }
-  }
+  // dims 16 (gq % 2) .. + 15 of each 32-dim block d; source lane src points at
+  // row key0 + src / 4, dims + 4 (src % 4)
+  const int gq = lane >> 4, src = lane & 15;
+  const int v_rd = grp_base + kKTileBytes + (4 * (gq >> 1) + (src >> 2)) * kVStride + 32 * (gq & 1) + 8 * (src & 3);
 
   f32x16_t o_acc[4];  // O^T, dim block d: lane holds query col, dims 32 d + 8 (i / 4) + 4 half + i % 4
 #pragma unroll
@@ -212,129 +207,159 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
     for (int i = 0; i < 16; ++i) o_acc[d][i] = 0.f;
   float m = kEmptyMax, lsum = 0.f;
 
-  if (n_tiles > 0) {
-    fetch(0);
+  if (t_first < t_end) {
+    fetch(t_first);
     stash(0);
   }
   __syncthreads();
 
-  // one 64-key tile on LDS buffer `buf` (a compile-time constant, so the
-  // buffer offset folds into the LDS instruction immediates)
+  // One iteration: this group's tile t_first + i on LDS buffer `buf`.
   // bufc / diagc are std::integral_constant in the main loop (the buffer
   // offset then folds into the LDS instruction immediates) and plain values
-  // for the few diagonal tiles at the end.
-  auto tile_step = [&](auto bufc, auto diagc, int t) {
+  // for the few tiles at the end.
+  auto tile_step = [&](auto bufc, auto diagc, int i) {
     const int buf = static_cast<int>(bufc);
-    const bool diag = static_cast<bool>(diagc);  // tile reaches past some row's position
-    if (t + 1 < n_tiles) fetch(t + 1);
-
-    // S^T for keys 64 t + 32 blk + (0..31)
-    f32x16_t s[2];
+    const int t = t_first + i;
+    const bool valid = t < t_end;
+    const bool prefetch = t + 1 < t_end;
+    if (prefetch) fetch(t + 1);
+    if (valid) {
+      const bool diag = static_cast<bool>(diagc) && t >= n_plain;
+      // S^T for keys 64 t + 32 blk + (0..31)
+      f32x16_t s[2];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      f32x16_t acc;
+      for (int blk = 0; blk < 2; ++blk) {
+        f32x16_t acc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+        for (int i2 = 0; i2 < 16; ++i2) acc[i2] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(&s_k[buf][k_off[blk][kk]]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qb[kk], acc, 0, 0, 0);
-      }
-      s[blk] = acc;
-    }
-
-    // scale, causal mask, running max (log2 domain)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = s[blk][i] * p.scale_log2;
-        if (diag) {
-          const int key = t * kKeysPerTile + 32 * blk + 8 * (i / 4) + 4 * half + (i % 4);
-          if (key > pos || !q_valid) v = -INFINITY;
+        for (int kk = 0; kk < 8; ++kk) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(
+              &lds[k_rd + buf * kBufBytes + blk * 32 * kKStride + kk * 32]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qb[kk], acc, 0, 0, 0);
         }
-        s[blk][i] = v;
-        mx = fmaxf(mx, v);
+        s[blk] = acc;
       }
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    if (__any(mx > m + kRescaleSlack)) {
-      if (mx > m + kRescaleSlack) {
-        const float a = fast_exp2(m - mx);
-        m = mx;
-        lsum *= a;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o_acc[d][i] *= a;
-      }
-    }
 
-    // P^T (bf16) for k-step (blk, tau): this lane's S^T entries 8 tau .. 8 tau + 7
-    bf16x8_t pb[2][2];
+      // scale, causal mask, running max (log2 domain)
+      float mx = -INFINITY;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        uint4 w;
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          e[j] = fast_exp2(s[blk][8 * tau + j] - m);
-          lsum += e[j];
+        for (int i2 = 0; i2 < 16; ++i2) {
+          float v = s[blk][i2] * p.scale_log2;
+          if (diag) {
+            const int key = t * kKeysPerTile + 32 * blk + 8 * (i2 / 4) + 4 * half + (i2 % 4);
+            if (key > pos || !q_valid) v = -INFINITY;
+          }
+          s[blk][i2] = v;
+          mx = fmaxf(mx, v);
         }
-        w.x = pack_bf16x2(e[0], e[1]);
-        w.y = pack_bf16x2(e[2], e[3]);
-        w.z = pack_bf16x2(e[4], e[5]);
-        w.w = pack_bf16x2(e[6], e[7]);
-        pb[blk][tau] = as_bf16x8(w);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
-
-    // O^T += V^T P^T
+      if (__any(mx > m + kRescaleSlack)) {
+        if (mx > m + kRescaleSlack) {
+          const float a = fast_exp2(m - mx);
+          m = mx;
+          lsum *= a;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+          for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(&s_v[buf][v_off[blk][tau][d][0]]));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(&s_v[buf][v_off[blk][tau][d][1]]));
-          // move whole dwords: element-wise 16-bit extraction here is lowered
-          // into half-word shuffles that drop the upper dword of each read
-          const uint2 l2 = __builtin_bit_cast(uint2, lo);
-          const uint2 h2 = __builtin_bit_cast(uint2, hi);
-          const bf16x8_t va = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
-          o_acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][tau], o_acc[d], 0, 0, 0);
+            for (int i2 = 0; i2 < 16; ++i2) o_acc[d][i2] *= a;
         }
       }
 
+      // P^T (bf16) for k-step (blk, tau): this lane's S^T entries 8 tau .. 8 tau + 7
+      bf16x8_t pb[2][2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          uint4 w;
+          float e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            e[j] = fast_exp2(s[blk][8 * tau + j] - m);
+            lsum += e[j];
+          }
+          w.x = pack_bf16x2(e[0], e[1]);
+          w.y = pack_bf16x2(e[2], e[3]);
+          w.z = pack_bf16x2(e[4], e[5]);
+          w.w = pack_bf16x2(e[6], e[7]);
+          pb[blk][tau] = as_bf16x8(w);
+        }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int o = v_rd + buf * kBufBytes + (32 * blk + 16 * tau) * kVStride + 64 * d;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(&lds[o]));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(&lds[o + 8 * kVStride]));
+            // move whole dwords: element-wise 16-bit extraction here is lowered
+            // into half-word shuffles that drop the upper dword of each read
+            const uint2 l2 = __builtin_bit_cast(uint2, lo);
+            const uint2 h2 = __builtin_bit_cast(uint2, hi);
+            const bf16x8_t va = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+            o_acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][tau], o_acc[d], 0, 0, 0);
+          }
+        }
+    }
     // buffer buf ^ 1 was last read in the previous iteration, which every wave
     // finished before that iteration's barrier
-    if (t + 1 < n_tiles) stash(buf ^ 1);
+    if (prefetch) stash(buf ^ 1);
     __syncthreads();
   };
-  // tiles below n_plain end at or before every row's position and need no mask
-  const int n_plain = min(n_tiles, diag_from / kKeysPerTile);
+
+  // main loop: both groups' tiles exist and need no mask
+  const int n_iter = nA;
+  const int n_main = max(0, S::KS == 2 ? min(nA, n_plain - nA) : n_plain);
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   using Plain = std::false_type;
-  int t = 0;
-  for (; t + 1 < n_plain; t += 2) {
-    tile_step(B0{}, Plain{}, t);
-    tile_step(B1{}, Plain{}, t + 1);
+  int i = 0;
+  for (; i + 1 < n_main; i += 2) {
+    tile_step(B0{}, Plain{}, i);
+    tile_step(B1{}, Plain{}, i + 1);
   }
-  for (; t < n_tiles; ++t) tile_step(t & 1, t >= n_plain, t);
+  for (; i < n_iter; ++i) tile_step(i & 1, true, i);
 
-  // combine the two lane halves of each query's sum, normalise, write
+  // combine the two lane halves of each query's sum
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
     lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
+  if (S::KS == 2) {
+    // group 1 hands (m, lsum, O^T) to group 0 through LDS (tiles are done)
+    float* xs = reinterpret_cast<float*>(lds) + (wave * 64 + lane) * 66;
+    if (grp == 1) {
+      xs[0] = m;
+      xs[1] = lsum;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) xs[2 + 16 * d + i2] = o_acc[d][i2];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xs[0], l1 = xs[1];
+    const float M = fmaxf(m, m1);
+    const float f0 = fast_exp2(m - M), f1 = fast_exp2(m1 - M);
+    lsum = lsum * f0 + l1 * f1;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) o_acc[d][i2] = o_acc[d][i2] * f0 + xs[2 + 16 * d + i2] * f1;
+    m = M;
+  }
+
   if (!q_valid) return;
   const bool empty = !(lsum > 0.f);
   const float inv = empty ? 0.f : 1.f / lsum;
