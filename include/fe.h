@@ -120,11 +120,16 @@ int fe_paged_gqa_decode_num_partitions(int B, int Hq, int Hkv, int D, int max_co
  *                 many block-aligned ranges of equal size; each is reduced
  *                 to a normalised fp32 partial and an LSE, and a second
  *                 kernel merges them by log-sum-exp.  0 = automatic, 1 = one
- *                 pass with no workspace.
+ *                 pass with no workspace.  A range holds at most 256 blocks
+ *                 (4096 tokens): a smaller value is raised to meet that, and
+ *                 a value above the longest context's block count is lowered
+ *                 (fe_paged_gqa_decode_num_partitions returns the value used).
  *   workspace     device scratch of at least
  *                 fe_paged_gqa_decode_workspace_size(...) bytes (may be NULL
- *                 when that size is 0); owned by the caller, contents
- *                 clobbered.
+ *                 when that size is 0), owned by the caller; contents are
+ *                 clobbered and need no initialisation.  Calls that may
+ *                 overlap in time (different streams) need different
+ *                 workspaces.
  * Source: ForgeEngine README, "What it implements" (CUDA paged GQA kernel);
  * "Make the Engine Talk" section 1.2 (one pass per generated token) and
  * section 1.3 (grouped-query attention).

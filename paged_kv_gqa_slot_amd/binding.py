@@ -122,8 +122,8 @@ def fe_paged_gqa_decode_num_partitions(B, Hq, Hkv, D, max_context_len, num_parti
 
 def fe_paged_gqa_decode(out, lse, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
                         scale: float, num_partitions: int = 0, workspace=None, stream=None) -> None:
-    """Decode attention; ``workspace`` (uint8 device tensor) is allocated by
-    torch when not given."""
+    """Decode attention.  ``workspace`` is a uint8 device tensor of at least
+    fe_paged_gqa_decode_workspace_size() bytes; one is allocated when not given."""
     B, Hq, D = q.shape
     NB, Hkv, BS, _ = k_cache.shape
     ws_bytes = fe_paged_gqa_decode_workspace_size(B, Hq, Hkv, D, max_context_len, num_partitions)

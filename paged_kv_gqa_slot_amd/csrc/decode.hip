@@ -203,37 +203,29 @@ __device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint3
 }
 
 template <int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 2))) void gqa_decode_partition_kernel(
-    DecodeParams p) {
-  __shared__ int s_bt[kMaxPartBlocks];
-  __shared__ float s_o[kWaves][G][kHeadDim];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
+struct DecodeShared {
+  float o[kWaves][G][kHeadDim];
+  float m[kWaves][G];
+  float l[kWaves][G];
+};
 
+// One work item: (sequence b, KV head g, partition part).
+template <int G>
+__device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<G>& sh, int b, int g, int part) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int r = lane >> 4, c = lane & 15;
 
-  int wg = blockIdx.x;
-  const int g = wg % p.Hkv;
-  wg /= p.Hkv;
-  const int part = wg % p.P;
-  const int b = wg / p.P;
-  const int L = clamp_len(p.context_lens[b], p.ctx_cap);
-  const int nblk = (L + kBlockSize - 1) / kBlockSize;
   const int blk0 = part * p.part_blocks;
-  if (blk0 >= nblk && p.P > 1) return;  // nothing here; pass 2 never reads this partition
-  const int blk1 = min(nblk, blk0 + p.part_blocks);
-  const int nb = max(0, blk1 - blk0);
-  // tokens in the sequence's last block; that block is masked if partial
-  const int rem = L - (nblk - 1) * kBlockSize;
-  const bool has_tail = nb > 0 && blk1 == nblk && rem < kBlockSize;
-  const int nfull = nb - (has_tail ? 1 : 0);
 
+  // Issued together, before the context length is known: the length, this
+  // wave's block ids (lane k <- local block wave + 4 k, i.e. the wave's tile
+  // k; a partition has at most kMaxPartBlocks = 4 * 64 blocks) and q.
+  const int Lraw = p.context_lens[b];
+  const int row_blocks = min(p.part_blocks, p.max_blocks - blk0);  // table entries this partition may use
   const int32_t* bt = p.block_tables + static_cast<size_t>(b) * p.max_blocks + blk0;
-  for (int i = tid; i < nb; i += kThreads) s_bt[i] = min(max(bt[i], 0), p.num_blocks - 1);
-
+  int ids = wave + kWaves * lane < row_blocks ? bt[wave + kWaves * lane] : 0;
   const size_t row0 = static_cast<size_t>(b) * p.Hq + static_cast<size_t>(g) * G;  // first q head of the group
   uint32_t qw[G][4];
   {
@@ -241,7 +233,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4
 #pragma unroll
     for (int h = 0; h < G; ++h) words4(qp[h * (kHeadDim / 8)], qw[h]);
   }
-  __syncthreads();
+  ids = min(max(ids, 0), p.num_blocks - 1);
+
+  const int L = clamp_len(Lraw, p.ctx_cap);
+  const int nblk = (L + kBlockSize - 1) / kBlockSize;
+  if (blk0 >= nblk && p.P > 1) return;  // nothing here; pass 2 never reads this partition
+  const int blk1 = min(nblk, blk0 + p.part_blocks);
+  const int nb = max(0, blk1 - blk0);
+  // tokens in the sequence's last block; that block is masked if partial
+  const int rem = L - (nblk - 1) * kBlockSize;
+  const bool has_tail = nb > 0 && blk1 == nblk && rem < kBlockSize;
+  const int nfull = nb - (has_tail ? 1 : 0);
 
   State<G> st;
 #pragma unroll
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4
   const int n = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
   auto issue = [&](Tile& dst, int t) {
     const bool ok = t < n;
-    const size_t o = ok ? static_cast<size_t>(uniform(s_bt[wave + t * kWaves])) * blk_stride : 0;
+    const size_t o = ok ? static_cast<size_t>(__builtin_amdgcn_readlane(ids, t)) * blk_stride : 0;
     const int bytes = ok ? kTileElems * 2 : 0;
     load_tile(dst, tile_rsrc(kg + o, bytes), tile_rsrc(vg + o, bytes), lane);
   };
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4
     }
   }
   if (has_tail && wave == (nb - 1) % kWaves) {
-    const size_t o = static_cast<size_t>(uniform(s_bt[nb - 1])) * blk_stride;
+    const size_t o = static_cast<size_t>(__builtin_amdgcn_readlane(ids, (nb - 1) / kWaves)) * blk_stride;
     const int bytes = rem * kHeadDim * 2;
     load_tile(ring[0], tile_rsrc(kg + o, bytes), tile_rsrc(vg + o, bytes), lane);
     consume<G, true>(st, ring[0], qw, p.scale_log2, r, rem);
@@ -308,15 +310,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4
   if (r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float4* dst = reinterpret_cast<float4*>(&s_o[wave][h][8 * c]);
+      float4* dst = reinterpret_cast<float4*>(&sh.o[wave][h][8 * c]);
       dst[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
       dst[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
     }
     if (c == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        s_m[wave][h] = st.m[h];
-        s_l[wave][h] = st.l[h];
+        sh.m[wave][h] = st.m[h];
+        sh.l[wave][h] = st.l[h];
       }
     }
   }
@@ -325,15 +327,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4
   // merge the 4 waves and write
   for (int o = tid; o < G * kHeadDim; o += kThreads) {
     const int h = o / kHeadDim, d = o % kHeadDim;
-    float M = s_m[0][h];
+    float M = sh.m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.m[w][h]);
     float lsum = 0.f, val = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(s_m[w][h] - M);
-      lsum = fmaf(s_l[w][h], f, lsum);
-      val = fmaf(s_o[w][h][d], f, val);
+      const float f = fast_exp2(sh.m[w][h] - M);
+      lsum = fmaf(sh.l[w][h], f, lsum);
+      val = fmaf(sh.o[w][h][d], f, val);
     }
     const bool empty = !(lsum > 0.f);
     const float res = empty ? 0.f : val / lsum;
@@ -347,6 +349,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4
       if (d == 0) p.lse_part[row * p.P + part] = lse_nat;
     }
   }
+}
+
+// Pass 1, one workgroup per item (grid B * P * Hkv, Hkv fastest).
+template <int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 2))) void gqa_decode_partition_kernel(
+    DecodeParams p) {
+  __shared__ DecodeShared<G> sh;
+  int wg = blockIdx.x;
+  const int g = wg % p.Hkv;
+  wg /= p.Hkv;
+  const int part = wg % p.P;
+  decode_item<G>(p, sh, wg / p.P, g, part);
 }
 
 // Pass 2: one wave per (sequence, query head); lane k owns dims 2k, 2k + 1.
@@ -384,11 +398,11 @@ __global__ __launch_bounds__(256) void gqa_decode_merge_kernel(const float* __re
 
 template <int G>
 hipError_t launch_g(const DecodeParams& prm, hipStream_t stream) {
-  const unsigned grid = static_cast<unsigned>(prm.B) * prm.P * prm.Hkv;
+  const long items = static_cast<long>(prm.B) * prm.P * prm.Hkv;
   DecodeParams copy = prm;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gqa_decode_partition_kernel<G>), dim3(grid),
-                         dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gqa_decode_partition_kernel<G>),
+                         dim3(static_cast<unsigned>(items)), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace
@@ -396,7 +410,7 @@ hipError_t launch_g(const DecodeParams& prm, hipStream_t stream) {
 bool plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_partitions, DecodePlan* plan) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_context_len < 0 || num_partitions < 0) return false;
   const int nblk_max = (max_context_len + kBlockSize - 1) / kBlockSize;
-  DecodePlan r{1, kMaxPartBlocks, 0, 0};
+  DecodePlan r{1, kMaxPartBlocks, 0, 0, 0};
   if (nblk_max > 0 && B > 0) {
     int P;
     if (num_partitions > 0) {
@@ -419,9 +433,10 @@ bool plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_partitions
     P = (nblk_max + part_blocks - 1) / part_blocks;
     r.partitions = P;
     r.part_blocks = part_blocks;
-    if (P > 1) {
+    if (P > 1) {  // [o_part fp32 rows x D][lse_part fp32 rows]
       const size_t rows = static_cast<size_t>(B) * Hq * P;
       const size_t o_bytes = (rows * kHeadDim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+      r.o_part_offset = 0;
       r.lse_part_offset = o_bytes;
       r.workspace_bytes = o_bytes + ((rows * sizeof(float) + 255) & ~static_cast<size_t>(255));
     }
@@ -451,7 +466,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.part_blocks = a.plan.part_blocks;
   prm.scale_log2 = a.scale * kLog2e;
   if (prm.P > 1) {
-    prm.o_part = static_cast<float*>(a.workspace);
+    prm.o_part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + a.plan.o_part_offset);
     prm.lse_part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + a.plan.lse_part_offset);
   }
   hipError_t e;

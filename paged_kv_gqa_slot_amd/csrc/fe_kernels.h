@@ -18,11 +18,13 @@ struct DecodePlan {
   int partitions;
   int part_blocks;
   size_t workspace_bytes;
-  size_t lse_part_offset;  // byte offset of the fp32 LSE partials in the workspace
+  size_t o_part_offset;    // byte offsets in the workspace of the fp32 partial outputs
+  size_t lse_part_offset;  // ... and of their LSEs
 };
 
-// Largest partition the decode kernel supports (block ids staged in LDS).
-constexpr int kMaxPartBlocks = 1024;
+// Largest decode partition: 256 KV blocks (4096 tokens), i.e. at most 64
+// tiles per wave, whose block ids one VGPR holds.
+constexpr int kMaxPartBlocks = 256;
 
 // Returns false for sizes the decode kernel cannot plan (non-positive sizes).
 bool plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_partitions, DecodePlan* plan);

@@ -158,3 +158,23 @@ def test_decode_qwen3_4b_b64(dev, seed):
 def test_decode_qwen3_4b_b8_ctx32768(dev):
     w = inputs.make("qwen3_4b_b8_ctx32768", poison="nan")
     run_decode(w, dev, parts=(8, 16, 32, 0), label="4b b8 32k")
+
+
+def test_decode_workspace_reuse(dev):
+    """One workspace, never cleared, serves many calls with various partition
+    counts; every result matches."""
+    lens = [700, 1500, 64, 999, 3000, 17]
+    w = inputs.custom("decode", 6, 32, 8, lens, 77, append=1)
+    dw = DeviceWorkload(w, dev)
+    rk, rv = dw.append()
+    ro, rl = oracle.decode(dw.lay.q, rk, rv, w.block_tables, w.context_lens, w.scale)
+    parts = (0, 4, 8, 2, 16, 4, 0)
+    size = max(fe.fe_paged_gqa_decode_workspace_size(6, 32, 8, 128, w.max_context_len, P) for P in parts)
+    ws = torch.full((size,), 0xA5, dtype=torch.uint8, device=dev)  # garbage must not matter
+    for P in parts:
+        out = torch.full((6, 32, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+        lse = torch.full((6, 32), float("nan"), dtype=torch.float32, device=dev)
+        fe.fe_paged_gqa_decode(out, lse, dw.q, dw.kc, dw.vc, dw.bt, dw.lens, w.max_context_len, w.scale,
+                               num_partitions=P, workspace=ws)
+        torch.cuda.synchronize()
+        assert_attention(out, lse, ro, rl, f"reuse P={P}")
