@@ -18,7 +18,9 @@
 //   16 lanes of a row.  Each row keeps its own online-softmax state (running
 //   max m, sum l, acc[G][8]) in the log2 domain; the max is only raised when
 //   it grows by more than 8 (so exp2 stays <= 256 and the rescale of acc is
-//   rare).  PV: fp32 FMA on the unpacked V row.  A partially filled last
+//   rare).  PV: v_dot2_f32_bf16 with the softmax weights of two tokens
+//   packed as a bf16 pair against the matching V words (fp32
+//   accumulation).  A partially filled last
 //   block is handled after the main loop by a masked variant of the same step.
 //
 // At the end the 4 rows and 4 waves are merged (max-shifted sums) through
@@ -68,7 +70,8 @@ struct DecodeParams {
   float* lse_part;
   int max_blocks, B, Hq, Hkv, num_blocks, ctx_cap;
   int P, part_blocks;
-  float scale_log2;
+  float scale_log2;  // |scale| * log2(e)
+  int negate_q;      // scale < 0
 };
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
@@ -136,6 +139,7 @@ struct State {
 template <int G, bool kTail>
 __device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint32_t (&qw)[G][4], float scale_log2,
                                         int r, int rem) {
+  // raw scores q.k (scale_log2 > 0: a negative scale was folded into q's sign)
   float s[4][G];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -146,13 +150,9 @@ __device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint3
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) a = dot2_bf16(qw[h][i], kw[i], a);
-      s[j][h] = a;
+      s[j][h] = sum16(a);
     }
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int h = 0; h < G; ++h) s[j][h] = sum16(s[j][h]) * scale_log2;
   if (kTail) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -164,7 +164,7 @@ __device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint3
   float mx[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    mx[h] = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
+    mx[h] = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h])) * scale_log2;
     need |= mx[h] > st.m[h] + kRescaleSlack;
   }
   if (__any(need)) {
@@ -179,24 +179,32 @@ __device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint3
       }
     }
   }
-  float p[4][G];
+  // p = 2^(s * scale_log2 - m); the PV product takes p in bf16 pairs
+  // (tokens r + 8 u and r + 8 u + 4 share a pair) with fp32 accumulation
+  uint32_t pp[2][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    float p[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j][h] = fast_exp2(s[j][h] - st.m[h]);
-    st.l[h] += (p[0][h] + p[1][h]) + (p[2][h] + p[3][h]);
+    for (int j = 0; j < 4; ++j) p[j] = fast_exp2(fmaf(s[j][h], scale_log2, -st.m[h]));
+    st.l[h] += (p[0] + p[1]) + (p[2] + p[3]);
+    pp[0][h] = pack_bf16x2(p[0], p[1]);
+    pp[1][h] = pack_bf16x2(p[2], p[3]);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t vw[4];
-    words4(t.v[j], vw);
+  for (int u = 0; u < 2; ++u) {
+    uint32_t va[4], vb[4];
+    words4(t.v[2 * u], va);
+    words4(t.v[2 * u + 1], vb);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float v0 = bf16_lo(vw[i]), v1 = bf16_hi(vw[i]);
+      // (dim 2i of both tokens) and (dim 2i + 1 of both tokens) as bf16 pairs
+      const uint32_t even = (va[i] & 0xffffu) | (vb[i] << 16);
+      const uint32_t odd = (va[i] >> 16) | (vb[i] & 0xffff0000u);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        st.acc[h][2 * i] = fmaf(p[j][h], v0, st.acc[h][2 * i]);
-        st.acc[h][2 * i + 1] = fmaf(p[j][h], v1, st.acc[h][2 * i + 1]);
+        st.acc[h][2 * i] = dot2_bf16(pp[u][h], even, st.acc[h][2 * i]);
+        st.acc[h][2 * i + 1] = dot2_bf16(pp[u][h], odd, st.acc[h][2 * i + 1]);
       }
     }
   }
@@ -232,6 +240,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<
     const uint4* qp = reinterpret_cast<const uint4*>(p.q + row0 * kHeadDim) + c;
 #pragma unroll
     for (int h = 0; h < G; ++h) words4(qp[h * (kHeadDim / 8)], qw[h]);
+    if (p.negate_q) {  // scale < 0: flip q's signs (exact) and use |scale|
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qw[h][i] ^= 0x80008000u;
+    }
   }
   ids = min(max(ids, 0), p.num_blocks - 1);
 
@@ -464,7 +478,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.ctx_cap = static_cast<int>(a.max_context_len < cap_bt ? a.max_context_len : cap_bt);
   prm.P = a.plan.partitions;
   prm.part_blocks = a.plan.part_blocks;
-  prm.scale_log2 = a.scale * kLog2e;
+  prm.scale_log2 = fabsf(a.scale) * kLog2e;
+  prm.negate_q = a.scale < 0.f;
   if (prm.P > 1) {
     prm.o_part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + a.plan.o_part_offset);
     prm.lse_part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + a.plan.lse_part_offset);

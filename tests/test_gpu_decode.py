@@ -178,3 +178,10 @@ def test_decode_workspace_reuse(dev):
                                num_partitions=P, workspace=ws)
         torch.cuda.synchronize()
         assert_attention(out, lse, ro, rl, f"reuse P={P}")
+
+
+def test_decode_negative_scale(dev):
+    """A negative softmax scale is folded into q's sign bits; results follow the definition."""
+    w = inputs.custom("decode", 3, 16, 4, [300, 47, 1000], 78, append=1)
+    w.scale = -w.scale
+    run_decode(w, dev, parts=(1, 4, 0), label="negative scale")
