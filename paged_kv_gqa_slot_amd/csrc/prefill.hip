@@ -25,9 +25,16 @@
 // accumulator layout leaves in each lane (no data movement for P).
 // LDS rows are padded (K: 272 bytes, V: 288 bytes) so that the K row reads of
 // 16 consecutive keys and the 4-key transposed V reads are free of bank
-// conflicts, and every LDS offset is a per-lane base plus a constant.  Each
-// group's K/V tiles are double-buffered: the next tile's global loads are
-// issued before the current tile's math.
+// conflicts, and every LDS offset is a per-lane base plus a constant.
+//
+// Schedule.  A tile's work is split into two phases separated by workgroup
+// barriers: an MFMA phase (S^T of tile i, then O^T += V^T P^T of tile i - 1)
+// and a VALU/memory phase (softmax of tile i into P, staging tile i + 1 into
+// LDS, issuing the global loads of tile i + 2).  Each group double-buffers
+// its K/V tiles in LDS.  With two groups the second
+// runs one phase behind the first, so on every SIMD one wave's MFMAs overlap
+// the other wave's softmax instead of both waves contending for the same unit
+// at the same time.
 #include <math.h>
 
 #include <type_traits>
@@ -63,7 +70,8 @@ struct PrefillParams {
   uint16_t* out;
   float* lse;
   int max_blocks, B, total_q, max_q_len, Hq, Hkv, num_blocks, ctx_cap, qtiles;
-  float scale_log2;
+  float scale_log2;  // |scale| * log2(e)
+  int negate_q;      // scale < 0: q's signs are flipped on load (exact)
 };
 
 template <int G>
@@ -121,8 +129,16 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
   bf16x8_t qb[8];
   {
     const uint4* qp = reinterpret_cast<const uint4*>(p.q + (static_cast<size_t>(q0 + qi) * p.Hq + head) * kHeadDim);
+    const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qb[kk] = as_bf16x8(q_valid ? qp[2 * kk + half] : make_uint4(0, 0, 0, 0));
+    for (int kk = 0; kk < 8; ++kk) {
+      uint4 w = q_valid ? qp[2 * kk + half] : make_uint4(0, 0, 0, 0);
+      w.x ^= flip;
+      w.y ^= flip;
+      w.z ^= flip;
+      w.w ^= flip;
+      qb[kk] = as_bf16x8(w);
+    }
   }
 
   // keys this workgroup needs: 0 .. last visible position of its last query
@@ -151,14 +167,33 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
   const int st_k = grp_base + (lane >> 4) * kKStride + (lane & 15) * 16;
   const int st_v = grp_base + kKTileBytes + (lane >> 4) * kVStride + (lane & 15) * 16;
   uint4 rk[S::kStageBlocks][4], rv[S::kStageBlocks][4];
-  auto fetch = [&](int t) {
+  // Block ids of the blocks this wave stages, held in VGPRs so a fetch needs
+  // no dependent scalar load: lane j of ids[i] holds the (clamped) id of
+  // block wave + i W of local tile 64 chunk + j, or 0 past the context.
+  int ids[S::kStageBlocks];
+  int ids_chunk = -1;
+  auto load_ids = [&](int chunk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < S::kStageBlocks; ++i) {
+      const int bl = wave + i * S::W;
+      const int lt = 64 * chunk + lane;
+      const int gb = 4 * (t_first + lt) + bl;
+      int v = 0;
+      if (bl < 4 && lt < t_end - t_first && gb < nblk_seq) v = min(max(bt[gb], 0), p.num_blocks - 1);
+      ids[i] = v;
+    }
+    ids_chunk = chunk;
+  };
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+    const int lt = t - t_first;
+    if ((lt >> 6) != ids_chunk) load_ids(lt >> 6);
 #pragma unroll
     for (int i = 0; i < S::kStageBlocks; ++i) {
       const int bl = wave + i * S::W;
       if (bl < 4) {
         const int gb = 4 * t + bl;  // block index within the sequence
         const bool ok = gb < nblk_seq;
-        const int blk = ok ? min(max(bt[gb], 0), p.num_blocks - 1) : 0;
+        const int blk = __builtin_amdgcn_readlane(ids[i], lt & 63);
         const int rows = ok ? min(kBlockSize, L - gb * kBlockSize) : 0;
         const size_t o = static_cast<size_t>(blk) * blk_stride;
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
@@ -175,7 +210,9 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
       }
     }
   };
-  auto stash = [&](int buf) {
+  // the staged tile goes to LDS buffer `buf` (tile j of the group: buffer j % 2)
+  auto stash = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int i = 0; i < S::kStageBlocks; ++i) {
       const int bl = wave + i * S::W;
@@ -206,130 +243,177 @@ __global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(P
 #pragma unroll
     for (int i = 0; i < 16; ++i) o_acc[d][i] = 0.f;
   float m = kEmptyMax, lsum = 0.f;
+  const float sc = p.scale_log2;  // > 0
 
-  if (t_first < t_end) {
-    fetch(t_first);
-    stash(0);
-  }
-  __syncthreads();
+  f32x16_t s[2];      // S^T of the current tile: keys 32 blk + 8 (i / 4) + 4 half + i % 4, query col
+  bf16x8_t pb[2][2];  // P^T of the previous tile, k-step (blk, tau): S^T entries 8 tau .. 8 tau + 7
 
-  // One iteration: this group's tile t_first + i on LDS buffer `buf`.
-  // bufc / diagc are std::integral_constant in the main loop (the buffer
-  // offset then folds into the LDS instruction immediates) and plain values
-  // for the few tiles at the end.
-  auto tile_step = [&](auto bufc, auto diagc, int i) {
-    const int buf = static_cast<int>(bufc);
-    const int t = t_first + i;
-    const bool valid = t < t_end;
-    const bool prefetch = t + 1 < t_end;
-    if (prefetch) fetch(t + 1);
-    if (valid) {
-      const bool diag = static_cast<bool>(diagc) && t >= n_plain;
-      // S^T for keys 64 t + 32 blk + (0..31)
-      f32x16_t s[2];
+  // S^T = K Q^T for the tile in LDS buffer `buf`
+  auto qk = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    f32x16_t acc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) acc[blk][i2] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        f32x16_t acc;
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) acc[i2] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(
-              &lds[k_rd + buf * kBufBytes + blk * 32 * kKStride + kk * 32]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qb[kk], acc, 0, 0, 0);
-        }
-        s[blk] = acc;
+        const uint4 kv = *reinterpret_cast<const uint4*>(&lds[k_rd + buf * kBufBytes + blk * 32 * kKStride + kk * 32]);
+        acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qb[kk], acc[blk], 0, 0, 0);
       }
+    s[0] = acc[0];
+    s[1] = acc[1];
+  };
 
-      // scale, causal mask, running max (log2 domain)
-      float mx = -INFINITY;
+  // O^T += V^T P^T for the tile in LDS buffer `buf`
+  auto pv = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int o = v_rd + buf * kBufBytes + (32 * blk + 16 * tau) * kVStride + 64 * d;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(&lds[o]));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(&lds[o + 8 * kVStride]));
+          // move whole dwords: element-wise 16-bit extraction here is lowered
+          // into half-word shuffles that drop the upper dword of each read
+          const uint2 l2 = __builtin_bit_cast(uint2, lo);
+          const uint2 h2 = __builtin_bit_cast(uint2, hi);
+          const bf16x8_t va = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+          o_acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][tau], o_acc[d], 0, 0, 0);
+        }
+      }
+  };
+
+  // causal mask, running max and P = 2^(S sc - m) for absolute tile t
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    float mx = -INFINITY;
+    if (t >= n_plain) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int i2 = 0; i2 < 16; ++i2) {
-          float v = s[blk][i2] * p.scale_log2;
-          if (diag) {
-            const int key = t * kKeysPerTile + 32 * blk + 8 * (i2 / 4) + 4 * half + (i2 % 4);
-            if (key > pos || !q_valid) v = -INFINITY;
-          }
-          s[blk][i2] = v;
-          mx = fmaxf(mx, v);
-        }
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      if (__any(mx > m + kRescaleSlack)) {
-        if (mx > m + kRescaleSlack) {
-          const float a = fast_exp2(m - mx);
-          m = mx;
-          lsum *= a;
-#pragma unroll
-          for (int d = 0; d < 4; ++d)
-#pragma unroll
-            for (int i2 = 0; i2 < 16; ++i2) o_acc[d][i2] *= a;
-        }
-      }
-
-      // P^T (bf16) for k-step (blk, tau): this lane's S^T entries 8 tau .. 8 tau + 7
-      bf16x8_t pb[2][2];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-          uint4 w;
-          float e[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            e[j] = fast_exp2(s[blk][8 * tau + j] - m);
-            lsum += e[j];
-          }
-          w.x = pack_bf16x2(e[0], e[1]);
-          w.y = pack_bf16x2(e[2], e[3]);
-          w.z = pack_bf16x2(e[4], e[5]);
-          w.w = pack_bf16x2(e[6], e[7]);
-          pb[blk][tau] = as_bf16x8(w);
-        }
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const int o = v_rd + buf * kBufBytes + (32 * blk + 16 * tau) * kVStride + 64 * d;
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(&lds[o]));
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(&lds[o + 8 * kVStride]));
-            // move whole dwords: element-wise 16-bit extraction here is lowered
-            // into half-word shuffles that drop the upper dword of each read
-            const uint2 l2 = __builtin_bit_cast(uint2, lo);
-            const uint2 h2 = __builtin_bit_cast(uint2, hi);
-            const bf16x8_t va = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
-            o_acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][tau], o_acc[d], 0, 0, 0);
-          }
+          const int key = t * kKeysPerTile + 32 * blk + 8 * (i2 / 4) + 4 * half + (i2 % 4);
+          if (key > pos || !q_valid) s[blk][i2] = -INFINITY;
         }
     }
-    // buffer buf ^ 1 was last read in the previous iteration, which every wave
-    // finished before that iteration's barrier
-    if (prefetch) stash(buf ^ 1);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, s[blk][i2]);
+    mx *= sc;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    if (__any(mx > m + kRescaleSlack)) {
+      if (mx > m + kRescaleSlack) {
+        const float a = fast_exp2(m - mx);
+        m = mx;
+        lsum *= a;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int i2 = 0; i2 < 16; ++i2) o_acc[d][i2] *= a;
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          e[j] = fast_exp2(fmaf(s[blk][8 * tau + j], sc, -m));
+          lsum += e[j];
+        }
+        uint4 w;
+        w.x = pack_bf16x2(e[0], e[1]);
+        w.y = pack_bf16x2(e[2], e[3]);
+        w.z = pack_bf16x2(e[4], e[5]);
+        w.w = pack_bf16x2(e[6], e[7]);
+        pb[blk][tau] = as_bf16x8(w);
+      }
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const int n_g = t_end - t_first;  // this group's tiles
+
+  // MFMA phase of local tile i (LDS buffer bufc): S^T of tile i and, when
+  // pvc, O^T += V^T P^T of tile i - 1 (the other buffer).  One basic block;
+  // the scheduling groups keep six MFMA operands in flight from LDS so the
+  // read latency hides behind the MFMAs (16 K reads of 16 bytes for S^T, then
+  // two 8-byte transposed V reads per PV MFMA).
+  auto mphase = [&](auto bufc, auto pvc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    using Other = std::integral_constant<int, 1 - buf>;
+    qk(bufc);
+    if constexpr (decltype(pvc)::value) {
+      pv(Other{});
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int j = 0; j < 10; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 6; ++j) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+
+  // One local tile i (LDS buffer i % 2 == bufc): MFMA phase, barrier,
+  // VALU/memory phase, barrier.  The O rescale in the softmax sees O with
+  // tile i - 1 already accumulated, as the online softmax requires.
+  auto step = [&](auto bufc, auto pvc, int i) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    using Other = std::integral_constant<int, 1 - buf>;
+    mphase(bufc, pvc);
+    __syncthreads();
+    // tile i + 1 (loaded during the previous phases) goes to buffer `Other`,
+    // last read by this MFMA phase's PV, which every wave finished before the
+    // barrier above; then the staging registers take tile i + 2's loads
+    if (i + 1 < n_g) stash(Other{});
+    if (i + 2 < n_g) fetch(t_first + i + 2);
+    softmax(t_first + i);
     __syncthreads();
   };
 
-  // main loop: both groups' tiles exist and need no mask
-  const int n_iter = nA;
-  const int n_main = max(0, S::KS == 2 ? min(nA, n_plain - nA) : n_plain);
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  using Plain = std::false_type;
-  int i = 0;
-  for (; i + 1 < n_main; i += 2) {
-    tile_step(B0{}, Plain{}, i);
-    tile_step(B1{}, Plain{}, i + 1);
+  if (S::KS == 2 && grp == 1) __syncthreads();  // run one phase behind group 0
+  if (n_g > 0) {
+    fetch(t_first);
+    stash(B0{});
   }
-  for (; i < n_iter; ++i) tile_step(i & 1, true, i);
+  if (n_g > 1) fetch(t_first + 1);
+  __syncthreads();
+  if (n_g > 0) step(B0{}, std::false_type{}, 0);  // the first tile has no PV of a previous one
+  int i = 1;
+  for (; i + 1 < n_g; i += 2) {
+    step(B1{}, std::true_type{}, i);
+    step(B0{}, std::true_type{}, i + 1);
+  }
+  if (i < n_g) step(B1{}, std::true_type{}, i);
+  // the last tile's PV
+  if (n_g > 0) {
+    if ((n_g - 1) & 1)
+      pv(B1{});
+    else
+      pv(B0{});
+  }
+  if (S::KS == 2 && grp == 0) __syncthreads();
+  // equal barrier counts: group 1 may have one tile fewer than group 0
+  for (int k = 2 * n_g; k < 2 * nA; ++k) __syncthreads();
 
   // combine the two lane halves of each query's sum
   {
@@ -410,7 +494,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   prm.num_blocks = a.num_blocks;
   const long cap_bt = static_cast<long>(a.max_blocks_per_seq) * kBlockSize;
   prm.ctx_cap = static_cast<int>(a.max_context_len < cap_bt ? a.max_context_len : cap_bt);
-  prm.scale_log2 = a.scale * kLog2e;
+  prm.scale_log2 = fabsf(a.scale) * kLog2e;
+  prm.negate_q = a.scale < 0.f;
   switch (a.Hq / a.Hkv) {
     case 1: return launch_g<1>(prm, stream);
     case 2: return launch_g<2>(prm, stream);

@@ -80,6 +80,33 @@ def _ragged(spec, lens, chunks, seed, poison):
                            layers=[lay])
 
 
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_prefill_tile_counts(dev, G):
+    """Key ranges of 1 to 18 64-key tiles (odd and even counts, so the two
+    wave groups that split the keys get equal or unequal shares, or one gets
+    none) with chunks of 1 to 300 rows."""
+    lens = [64, 65, 128, 190, 257, 1000, 1088, 700]
+    chunks = [64, 1, 100, 190, 3, 300, 1, 129]
+    spec = inputs.Spec("prefill_ragged", "prefill", len(lens), 2 * G, 2, min(lens), max(lens), append=0, chunk=0)
+    w = _ragged(spec, lens, chunks, 400 + G, "nan")
+    run_prefill(w, dev, f"tile counts G={G}")
+
+
+@pytest.mark.parametrize("G,lens", [(4, [9000, 8300]), (8, [4500, 4200])])
+def test_prefill_long_key_range(dev, G, lens):
+    """More than 64 tiles of keys per wave group, so the kernel's per-wave
+    list of staged block ids is reloaded mid-sequence."""
+    w = inputs.custom("prefill", 2, 2 * G, 2, lens, 500 + G, append=64, chunk=64, poison="nan")
+    run_prefill(w, dev, f"long key range G={G}")
+
+
+def test_prefill_negative_scale(dev):
+    """A negative softmax scale is folded into q's sign bits; results follow the definition."""
+    w = inputs.custom("prefill", 2, 32, 8, [300, 97], 303, append=64, chunk=64, poison="nan")
+    w.scale = -w.scale
+    run_prefill(w, dev, "negative scale")
+
+
 def test_prefill_context_shorter_than_chunk(dev):
     """Rows whose position is negative see no key: out 0, lse -inf."""
     w = inputs.custom("prefill", 2, 8, 2, [40, 70], 301, append=40, chunk=40, poison="nan")
