@@ -10,6 +10,12 @@ blocks, context lengths 1024..8192 (seeded, synthetic).
 Prints one JSON line.  `value` is algorithmic HBM bytes per step / step time
 in GB/s; `roofline` is for the decode call, timed with HIP events on the
 stream its kernels run on; `cpu_baseline` is the fp64 oracle on the host.
+
+Other workloads (--workload): the chunked-prefill one reports TFLOP/s against
+the bf16 MFMA peak; the mixed one (decode rows and prefill chunks in one
+fe_paged_gqa_mixed launch) reports microseconds per step against the larger
+of its decode rows' HBM time and its prefill chunks' MFMA time, with the same
+work launched as two separate calls timed beside it.
 """
 import argparse
 import hashlib
@@ -45,14 +51,62 @@ def append_bytes(w) -> int:
     return T * w.Hkv * 128 * 2 * 2 * 2 + T * 4  # read new K/V, write into the pools, slots
 
 
-def prefill_flops(w) -> int:
-    """4*D flop per unmasked (query, key, head) triple (QK^T and PV)."""
+def prefill_flops(w, first: int = 0) -> int:
+    """4*D flop per unmasked (query, key, head) triple (QK^T and PV) of the
+    sequences from `first` on."""
     qsl = w.query_start_loc.tolist()
     tot = 0
     for b, L in enumerate(w.context_lens.tolist()):
+        if b < first:
+            continue
         C = qsl[b + 1] - qsl[b]
         tot += sum(L - C + i + 1 for i in range(C))
     return tot * w.Hq * 4 * 128
+
+
+def mixed_decode_bytes(w, nd: int) -> int:
+    """Algorithmic HBM bytes of the decode rows of a mixed batch (as decode_bytes)."""
+    lens = [int(x) for x in w.context_lens.tolist()[:nd]]
+    kv = sum(lens) * w.Hkv * 128 * 2 * 2
+    blocks = sum((L + 15) // 16 for L in lens)
+    return kv + nd * w.Hq * 128 * 2 * 2 + nd * w.Hq * 4 + blocks * 4 + nd * 4
+
+
+def time_separate_calls(fe, torch, w, x, nd, qsl, bt, lens, mcl, steps, stream) -> float:
+    """Milliseconds per step of the mixed batch's work launched as two calls:
+    fe_paged_gqa_decode on the decode rows, then fe_paged_gqa_prefill_chunk on
+    the chunks (same stream, no append)."""
+    dev = x["q"].device
+    qd = x["q"][:nd].contiguous()
+    qp = x["q"][nd:].contiguous()
+    qsl_p = (qsl[nd:] - nd).contiguous()
+    bt_d, bt_p = bt[:nd].contiguous(), bt[nd:].contiguous()
+    l_d, l_p = lens[:nd].contiguous(), lens[nd:].contiguous()
+    od = torch.empty(nd, w.Hq, 128, dtype=torch.bfloat16, device=dev)
+    ld = torch.empty(nd, w.Hq, dtype=torch.float32, device=dev)
+    op = torch.empty(qp.shape[0], w.Hq, 128, dtype=torch.bfloat16, device=dev)
+    lp = torch.empty(qp.shape[0], w.Hq, dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(fe.fe_paged_gqa_decode_workspace_size(nd, w.Hq, w.Hkv, 128, mcl, 0), 1), dtype=torch.uint8,
+                     device=dev)
+    chunks = [b - a for a, b in zip(qsl_p.tolist()[:-1], qsl_p.tolist()[1:])]
+    mql = max(chunks, default=0)
+
+    def two():
+        if nd:
+            fe.fe_paged_gqa_decode(od, ld, qd, x["kc"], x["vc"], bt_d, l_d, mcl, w.scale, workspace=ws)
+        if qp.shape[0]:
+            fe.fe_paged_gqa_prefill_chunk(op, lp, qp, qsl_p, x["kc"], x["vc"], bt_p, l_p, mql, mcl, w.scale)
+
+    for _ in range(3):
+        two()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        two()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
 
 
 def kernel_source_digest(kind: str) -> str:
@@ -125,6 +179,11 @@ def cpu_baseline(w, budget_s: float):
     if n > len(rows):
         rows, el = run(n)
     flops = sum(prefill_row_flops(w, r) for r in rows)
+    if w.spec.kind == "mixed":  # the whole step's time, scaled from the sample by flops
+        total = sum(prefill_row_flops(w, r) for r in range(total_q))
+        return {"value": round(total / (flops / el) * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
+                "sample": f"fp64 oracle on {len(rows)} of {total_q} query rows (decode rows and prefill chunks) "
+                          f"({el:.1f} s), scaled to the whole step by flops; append not included"}
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle prefill on {len(rows)} of {total_q} query rows spread over the chunk "
                       f"({el:.1f} s); flops counted for those rows"}
@@ -172,16 +231,28 @@ def main():
     out = torch.empty(total_q, w.Hq, 128, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(total_q, w.Hq, dtype=torch.float32, device=dev)
     is_decode = spec.kind == "decode"
-    P = fe.fe_paged_gqa_decode_num_partitions(w.B, w.Hq, w.Hkv, 128, mcl, args.partitions) if is_decode else 0
-    ws_bytes = fe.fe_paged_gqa_decode_workspace_size(w.B, w.Hq, w.Hkv, 128, mcl, args.partitions) if is_decode else 0
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    max_q = max(b - a for a, b in zip(w.query_start_loc.tolist()[:-1], w.query_start_loc.tolist()[1:])) if qsl is not None else 0
+    is_mixed = spec.kind == "mixed"
+    nd = spec.num_decode if is_mixed else 0
+    if is_decode:
+        P = fe.fe_paged_gqa_decode_num_partitions(w.B, w.Hq, w.Hkv, 128, mcl, args.partitions)
+        ws_bytes = fe.fe_paged_gqa_decode_workspace_size(w.B, w.Hq, w.Hkv, 128, mcl, args.partitions)
+    elif is_mixed:
+        ws_bytes = fe.fe_paged_gqa_mixed_workspace_size(nd, w.Hq, w.Hkv, 128, mcl, args.partitions)
+        P = args.partitions
+    else:
+        P, ws_bytes = 0, 0
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)  # zero-filled once (mixed: arrival counters)
+    chunks = [b - a for a, b in zip(w.query_start_loc.tolist()[:-1], w.query_start_loc.tolist()[1:])] if qsl is not None else []
+    max_q = max(chunks[nd:], default=0)
     do_append = slots.numel() > 0
 
     def attend(x):
         if is_decode:
             fe.fe_paged_gqa_decode(out, lse, x["q"], x["kc"], x["vc"], bt, lens, mcl, w.scale,
                                    num_partitions=args.partitions, workspace=ws)
+        elif is_mixed:
+            fe.fe_paged_gqa_mixed(out, lse, x["q"], qsl, x["kc"], x["vc"], bt, lens, nd, max_q, mcl, w.scale,
+                                  num_partitions=args.partitions, workspace=ws)
         else:
             fe.fe_paged_gqa_prefill_chunk(out, lse, x["q"], qsl, x["kc"], x["vc"], bt, lens, max_q, mcl, w.scale)
 
@@ -240,6 +311,23 @@ def main():
         extra = {"pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                  "kv_tokens_per_s": round(nl * w.kv_tokens / (ms_per_step * 1e-3), 1),
                  "decode_only_kv_tokens_per_s": round(w.kv_tokens / (att_avg_ms * 1e-3), 1)}
+    elif is_mixed:
+        dec_bytes = mixed_decode_bytes(w, nd)
+        flops = prefill_flops(w, first=nd)
+        t_hbm = dec_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+        t_mfma = flops / (MFMA_BF16_PEAK_TFS * 1e12) * 1e6
+        sep_us = time_separate_calls(fe, torch, w, L[0], nd, qsl, bt, lens, mcl, args.steps, stream) * 1e3
+        bound_us = max(t_hbm, t_mfma)
+        value = ms_per_step * 1e3
+        roof = {"bound": "hbm+mfma", "achieved": round(att_avg_ms * 1e3, 2), "peak": round(bound_us, 2), "unit": "us",
+                "frac": round(bound_us / (att_avg_ms * 1e3), 4), "traffic": None,
+                "kernel": "fe_paged_gqa_mixed (gqa_mixed_kernel)", "decode_rows_bytes": dec_bytes,
+                "prefill_flops": flops, "hbm_bound_us": round(t_hbm, 2), "mfma_bound_us": round(t_mfma, 2),
+                "separate_calls_us": round(sep_us, 2), "avg_ms": round(att_avg_ms, 5),
+                "median_ms": round(att_med_ms, 5)}
+        metric = "mixed decode+prefill step, one launch, microseconds per step, Qwen3-4B shape"
+        unit = "us"
+        extra = {}
     else:
         flops = prefill_flops(w)
         value = nl * flops / (ms_per_step * 1e-3) / 1e12
@@ -272,7 +360,8 @@ def main():
            "block_size": 16, "layers": nl, "kv_tokens": w.kv_tokens, "max_context_len": mcl,
            "append_tokens_per_step": int(slots.numel()) * nl, "num_partitions": P, "seed": w.seed}
     rec = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": not is_mixed,
+           "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg, **extra, "roofline": roof,
            "cpu_baseline": cpu}
     print(json.dumps(rec), flush=True)

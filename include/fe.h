@@ -44,8 +44,9 @@
  *   - Device-array contents are not checked on the host (that would need a
  *     synchronisation).  Kernels clamp instead of faulting: block ids are
  *     clamped into [0, num_blocks), context lengths into
- *     [0, min(max_context_len, max_blocks_per_seq * BS)], and append slots
- *     outside [0, num_blocks * BS) are skipped.  Out-of-contract contents
+ *     [0, min(max_context_len, max_blocks_per_seq * BS)], query rows named
+ *     by query_start_loc into [0, total_q), and append slots outside
+ *     [0, num_blocks * BS) are skipped.  Out-of-contract contents
  *     thus give unspecified results, never an out-of-bounds access.
  *   - Defined edge cases: a context length of 0 gives out = 0 and
  *     lse = -inf; block-table entries past ceil(L / BS) and pool slots past
@@ -164,6 +165,50 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
                                int max_blocks_per_seq, const int32_t* context_lens, int B, int total_q,
                                int max_q_len, int Hq, int Hkv, int D, int BS, int num_blocks,
                                int max_context_len, float scale, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fe_paged_gqa_mixed needs for these sizes
+ * (num_partitions 0 = automatic).  Host-only; 0 when no decode sequence is
+ * split, (size_t)-1 for invalid sizes.
+ */
+size_t fe_paged_gqa_mixed_workspace_size(int num_decode, int Hq, int Hkv, int D, int max_context_len,
+                                         int num_partitions);
+
+/*
+ * Mixed batch in ONE kernel launch: decode rows and prefill chunks together,
+ * the step a token-budgeted continuous batcher produces.
+ *   Sequences b in [0, num_decode) are decode rows: each owns exactly one
+ *   packed query row, query_start_loc[b], and attends over its whole context
+ *   (as fe_paged_gqa_decode).  Sequences b in [num_decode, B) are prefill
+ *   chunks (as fe_paged_gqa_prefill_chunk: bottom-right causal).  A decode
+ *   row is thus the chunk of length one of its sequence; results equal those
+ *   of the two separate calls within their tolerances.
+ *   out, lse, q, query_start_loc, k_cache, v_cache, block_tables,
+ *   context_lens, total_q, max_context_len, scale: as in
+ *   fe_paged_gqa_prefill_chunk, over all B sequences.
+ *   max_q_len      host-side upper bound of the prefill chunks' lengths
+ *   num_partitions split-K factor of the decode rows (0 = automatic: ranges
+ *                  of 64 blocks), at most 256 blocks per range as in decode
+ *   workspace      device scratch of at least
+ *                  fe_paged_gqa_mixed_workspace_size(...) bytes (NULL when
+ *                  that is 0), owned by the caller.  It must be zero-filled
+ *                  once before its first use: it starts with num_decode * Hkv
+ *                  arrival counters (the last partition of a split decode
+ *                  row to finish merges the partials in the same launch),
+ *                  which every completed call leaves at zero again; the rest
+ *                  is clobbered.  Calls that may overlap in time need
+ *                  different workspaces.
+ *   Preconditions on device contents (not checked): query_start_loc[b] = b
+ *   and query_start_loc[b + 1] - query_start_loc[b] = 1 for b < num_decode.
+ * Source: ForgeEngine README, "Scheduling" (continuous, token-budgeted
+ * batching) and "What it implements" (paged GQA kernel, restricted prefill
+ * lab); "Make the Engine Talk" section 1.2.
+ */
+int fe_paged_gqa_mixed(void* out, float* lse, const void* q, const int32_t* query_start_loc, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* context_lens, int B, int num_decode, int total_q, int max_q_len, int Hq,
+                       int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale, int num_partitions,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* fe_status_string(int status);

@@ -10,6 +10,8 @@ from .binding import (  # noqa: F401
     fe_paged_gqa_decode,
     fe_paged_gqa_decode_num_partitions,
     fe_paged_gqa_decode_workspace_size,
+    fe_paged_gqa_mixed,
+    fe_paged_gqa_mixed_workspace_size,
     fe_paged_gqa_prefill_chunk,
     fe_paged_kv_append,
     fe_status_string,

@@ -50,6 +50,10 @@ def load_library():
     lib.fe_paged_gqa_decode.restype = I
     lib.fe_paged_gqa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, P]
     lib.fe_paged_gqa_prefill_chunk.restype = I
+    lib.fe_paged_gqa_mixed_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.fe_paged_gqa_mixed_workspace_size.restype = Z
+    lib.fe_paged_gqa_mixed.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.fe_paged_gqa_mixed.restype = I
     lib.fe_status_string.argtypes = [I]
     lib.fe_status_string.restype = ctypes.c_char_p
     lib.fe_last_error.argtypes = []
@@ -153,3 +157,35 @@ def fe_paged_gqa_prefill_chunk(out, lse, q, query_start_loc, k_cache, v_cache, b
         block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens", 1), B, total_q, int(max_q_len),
         Hq, Hkv, D, BS, NB, int(max_context_len), float(scale), _stream(stream))
     _check(rc, "fe_paged_gqa_prefill_chunk")
+
+
+def fe_paged_gqa_mixed_workspace_size(num_decode, Hq, Hkv, D, max_context_len, num_partitions=0) -> int:
+    n = load_library().fe_paged_gqa_mixed_workspace_size(num_decode, Hq, Hkv, D, max_context_len, num_partitions)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("fe_paged_gqa_mixed_workspace_size: invalid sizes")
+    return int(n)
+
+
+def fe_paged_gqa_mixed(out, lse, q, query_start_loc, k_cache, v_cache, block_tables, context_lens, num_decode: int,
+                       max_q_len: int, max_context_len: int, scale: float, num_partitions: int = 0, workspace=None,
+                       stream=None) -> None:
+    """Decode rows (sequences [0, num_decode), one query row each) and prefill
+    chunks (the rest) in one launch.  ``workspace``: uint8 device tensor of at
+    least fe_paged_gqa_mixed_workspace_size() bytes, zero-filled before its
+    first use; one is allocated (zeroed) when not given."""
+    total_q, Hq, D = q.shape
+    NB, Hkv, BS, _ = k_cache.shape
+    B = context_lens.shape[0]
+    ws_bytes = fe_paged_gqa_mixed_workspace_size(num_decode, Hq, Hkv, D, max_context_len, num_partitions)
+    if workspace is None and ws_bytes:
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, torch.uint8, "workspace") if workspace is not None else None
+    ws_have = workspace.numel() if workspace is not None else 0
+    rc = load_library().fe_paged_gqa_mixed(
+        _dev(out, torch.bfloat16, "out", 3), _dev(lse, torch.float32, "lse", 2), _dev(q, torch.bfloat16, "q", 3),
+        _dev(query_start_loc, torch.int32, "query_start_loc", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
+        _dev(v_cache, torch.bfloat16, "v_cache", 4), _dev(block_tables, torch.int32, "block_tables", 2),
+        block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens", 1), B, int(num_decode), total_q,
+        int(max_q_len), Hq, Hkv, D, BS, NB, int(max_context_len), float(scale), int(num_partitions), ws_ptr, ws_have,
+        _stream(stream))
+    _check(rc, "fe_paged_gqa_mixed")

@@ -143,4 +143,47 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
   }
 }
 
+size_t fe_paged_gqa_mixed_workspace_size(int num_decode, int Hq, int Hkv, int D, int max_context_len,
+                                         int num_partitions) {
+  fe::MixedPlan plan;
+  if (D != fe::kHeadDim || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0) return static_cast<size_t>(-1);
+  if (!fe::plan_mixed(num_decode, Hq, Hkv, max_context_len, num_partitions, &plan)) return static_cast<size_t>(-1);
+  return plan.workspace_bytes;
+}
+
+int fe_paged_gqa_mixed(void* out, float* lse, const void* q, const int32_t* query_start_loc, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* context_lens, int B, int num_decode, int total_q, int max_q_len, int Hq,
+                       int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale, int num_partitions,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  static const char* fn = "fe_paged_gqa_mixed";
+  try {
+    if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+        num_partitions < 0)
+      return fail(FE_ERR_INVALID_ARG, fn,
+                  "B, total_q, max_q_len, max_context_len, num_partitions must be >= 0; num_blocks, "
+                  "max_blocks_per_seq positive");
+    if (num_decode < 0 || num_decode > B) return fail(FE_ERR_INVALID_ARG, fn, "num_decode must be in [0, B]");
+    if (num_decode > total_q) return fail(FE_ERR_INVALID_ARG, fn, "every decode row needs a query row (total_q)");
+    if (int rc = check_heads(fn, Hq, Hkv, D, BS)) return rc;
+    if (!isfinite(scale)) return fail(FE_ERR_INVALID_ARG, fn, "scale must be finite");
+    fe::MixedPlan plan;
+    if (!fe::plan_mixed(num_decode, Hq, Hkv, max_context_len, num_partitions, &plan))
+      return fail(FE_ERR_INVALID_ARG, fn, "cannot plan these sizes");
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+      return fail(FE_ERR_WORKSPACE, fn, "workspace missing or smaller than fe_paged_gqa_mixed_workspace_size()");
+    if (B == 0 || total_q == 0) return FE_OK;
+    if (!out || !q || !query_start_loc || !k_cache || !v_cache || !block_tables || !context_lens)
+      return fail(FE_ERR_NULL, fn,
+                  "out, q, query_start_loc, k_cache, v_cache, block_tables, context_lens must not be NULL");
+    fe::MixedArgs a{{out, lse, q, query_start_loc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale},
+                    num_decode, plan, workspace};
+    const hipError_t e = fe::launch_mixed(a, stream);
+    return e == hipSuccess ? FE_OK : hip_fail(e, fn);
+  } catch (...) {
+    return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
+  }
+}
+
 }  // extern "C"

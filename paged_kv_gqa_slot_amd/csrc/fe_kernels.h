@@ -58,9 +58,35 @@ struct PrefillArgs {
   float scale;
 };
 
+// Mixed decode/prefill launch plan.  The decode sequences are split into
+// `partitions` ranges of `part_blocks` blocks; their partials are merged in
+// the same launch by the last partition to finish, counted in the workspace:
+// [arrival counters int num_decode x Hkv][o_part fp32][lse_part fp32].
+struct MixedPlan {
+  int partitions;
+  int part_blocks;
+  size_t workspace_bytes;
+  size_t o_part_offset;
+  size_t lse_part_offset;
+};
+
+// Automatic decode partitions of a mixed launch: ranges of 64 blocks (1024
+// tokens), since the prefill tiles of the same grid already occupy the GPU.
+constexpr int kMixedAutoPartBlocks = 64;
+
+bool plan_mixed(int num_decode, int Hq, int Hkv, int max_context_len, int num_partitions, MixedPlan* plan);
+
+struct MixedArgs {
+  PrefillArgs all;  // the whole batch: sequences [0, num_decode) decode, the rest prefill chunks
+  int num_decode;
+  MixedPlan plan;
+  void* workspace;
+};
+
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_cache,
                             void* v_cache, int T, int num_blocks, int Hkv, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_mixed(const MixedArgs& a, hipStream_t stream);
 
 }  // namespace fe

@@ -1,0 +1,484 @@
+// Chunked-prefill query tile over the paged cache on the bf16 MFMA units,
+// shared by the prefill kernel and the mixed decode/prefill kernel
+// (ForgeEngine README, "What it implements": restricted prefill lab, and
+// "Scheduling": token-budgeted batching that cuts prompts into chunks; "Make
+// the Engine Talk" section 1.2: the prefill pass that primes the cache).
+//
+// A chunk of C queries sits at the end of its sequence: query i is at
+// position L - C + i and attends to keys 0 .. L - C + i.
+//
+// One workgroup per (sequence, KV head, tile of QT query rows).  W waves
+// each own 32 (query row, query head) pairs of the group -- one head per wave
+// when G >= 4 -- so every K/V tile staged in LDS is shared by all G heads.
+// When W <= 4 the workgroup has KS = 2 such wave groups that split the key
+// range in two halves (two waves per SIMD instead of one) and merge their
+// (max, sum, O) by log-sum-exp through LDS at the end.
+// Per 64-key tile each wave computes
+//   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
+//                      B = Q^T held in registers (32 queries x 128 dims)
+//   online softmax     the D layout puts query (lane % 32) in every lane, so
+//                      the row max/sum are lane-local plus one permlane32 swap
+//   O^T += V^T P^T     B = P^T packed to bf16 straight from the S^T registers;
+//                      A = V^T read from the row-major V tile with
+//                      ds_read_b64_tr_b16 (two 4-key transposed reads).
+// The MFMA sums over keys in any order as long as A and B agree, so the
+// k-slot -> key order of each PV step is chosen to match the keys the S^T
+// accumulator layout leaves in each lane (no data movement for P).
+// LDS rows are padded (K: 272 bytes, V: 288 bytes) so that the K row reads of
+// 16 consecutive keys and the 4-key transposed V reads are free of bank
+// conflicts, and every LDS offset is a per-lane base plus a constant.
+//
+// Schedule.  A tile's work is split into two phases separated by workgroup
+// barriers: an MFMA phase (S^T of tile i, then O^T += V^T P^T of tile i - 1)
+// and a VALU/memory phase (softmax of tile i into P, staging tile i + 1 into
+// LDS, issuing the global loads of tile i + 2).  Each group double-buffers
+// its K/V tiles in LDS.  With two groups the second runs one phase behind the
+// first, so on every SIMD one wave's MFMAs overlap the other wave's softmax
+// instead of both waves contending for the same unit at the same time.
+#pragma once
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "fe_device.h"
+#include "fe_kernels.h"
+
+namespace fe {
+namespace pre {
+
+constexpr int kKeysPerTile = 64;
+constexpr int kRowBytes = kHeadDim * 2;                 // 256 bytes of one K/V row
+constexpr int kKStride = kRowBytes + 16;                // padded LDS row strides
+constexpr int kVStride = kRowBytes + 32;
+constexpr int kKTileBytes = kKeysPerTile * kKStride;    // 17408
+constexpr int kVTileBytes = kKeysPerTile * kVStride;    // 18432
+constexpr int kBufBytes = kKTileBytes + kVTileBytes;    // one K + V tile
+constexpr float kRescaleSlack = 8.0f;
+constexpr float kEmptyMax = -1.0e30f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct PrefillParams {
+  const uint16_t* q;
+  const int32_t* query_start_loc;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  uint16_t* out;
+  float* lse;
+  int max_blocks, B, total_q, max_q_len, Hq, Hkv, num_blocks, ctx_cap, qtiles;
+  float scale_log2;  // |scale| * log2(e)
+  int negate_q;      // scale < 0: q's signs are flipped on load (exact)
+};
+
+template <int G>
+struct Shape {
+  static constexpr int W = (G <= 4 && 4 % G == 0) ? 4 : G;  // waves per group
+  static constexpr int KS = W <= 4 ? 2 : 1;                 // groups splitting the keys
+  static constexpr int QT = 32 * W / G;                     // query rows per workgroup
+  static constexpr int kThreads = 64 * W * KS;
+  // a 64-key tile is 4 KV blocks; wave w of a group stages blocks w, w + W, ...
+  static constexpr int kStageBlocks = (4 + W - 1) / W;
+  static constexpr int kLdsBytes = 2 * KS * kBufBytes;
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Query tile qt of sequence b against KV head g, run by the whole workgroup
+// (Shape<G>::kThreads threads); lds holds Shape<G>::kLdsBytes bytes.
+template <int G>
+__device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned char* lds, int qt, int b, int g) {
+  using S = Shape<G>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave_all = uniform(tid >> 6);
+  const int grp = wave_all / S::W;  // which half of the key range
+  const int wave = wave_all % S::W;
+  const int col = lane & 31;   // this lane's query within the wave's 32
+  const int half = lane >> 5;  // which 8-dim / 4-key half of an MFMA operand
+
+  const int q0 = p.query_start_loc[b];
+  int C = p.query_start_loc[b + 1] - q0;
+  C = C < 0 ? 0 : (C > p.max_q_len ? p.max_q_len : C);
+  const int i0 = qt * S::QT;
+  if (i0 >= C) return;
+  int L = p.context_lens[b];
+  L = L < 0 ? 0 : (L > p.ctx_cap ? p.ctx_cap : L);
+
+  // this wave's (head, query) rows: head h_loc, queries i0 + qoff .. + 31
+  const int h_loc = (wave * 32) / S::QT;
+  const int qoff = (wave * 32) % S::QT;
+  const int qi = i0 + qoff + col;              // this lane's query index in the chunk
+  const bool q_valid = qi < C && q0 + qi < p.total_q;
+  const int pos = L - C + qi;                  // its position; keys 0..pos are visible
+  const int head = g * G + h_loc;
+
+  // Q^T operand: k-step kk covers dims 16 kk .. 16 kk + 15; this lane holds 8.
+  bf16x8_t qb[8];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(p.q + (static_cast<size_t>(q0 + qi) * p.Hq + head) * kHeadDim);
+    const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      uint4 w = q_valid ? qp[2 * kk + half] : make_uint4(0, 0, 0, 0);
+      w.x ^= flip;
+      w.y ^= flip;
+      w.z ^= flip;
+      w.w ^= flip;
+      qb[kk] = as_bf16x8(w);
+    }
+  }
+
+  // keys this workgroup needs: 0 .. last visible position of its last query
+  const int last_q = min(i0 + S::QT, C) - 1;
+  const int kv_end = max(0, min(L, L - C + last_q + 1));
+  const int n_tiles = (kv_end + kKeysPerTile - 1) / kKeysPerTile;
+  const int diag_from = max(0, L - C + i0 + 1);  // keys beyond this need the causal mask for some row
+  const int n_plain = min(n_tiles, diag_from / kKeysPerTile);  // tiles needing no mask
+  // group 0 takes tiles [0, nA), group 1 tiles [nA, n_tiles)
+  const int nA = S::KS == 2 ? (n_tiles + 1) / 2 : n_tiles;
+  const int t_first = grp * nA;
+  const int t_end = grp == 0 ? nA : n_tiles;
+
+  const int32_t* bt = p.block_tables + static_cast<size_t>(b) * p.max_blocks;
+  const size_t blk_stride = static_cast<size_t>(p.Hkv) * kTileElems;
+  const uint16_t* kg = p.k_cache + static_cast<size_t>(g) * kTileElems;
+  const uint16_t* vg = p.v_cache + static_cast<size_t>(g) * kTileElems;
+  const int grp_base = grp * 2 * kBufBytes;
+
+  // Staging: wave w copies blocks w, w + W, ... of each 64-key tile, each a
+  // contiguous 4 KiB (block, KV head) run, lane reading 16 bytes at
+  // lane + 64 j (token row 4 j + lane / 16, chunk lane % 16).  Rows past the
+  // context come back as zeros from the buffer range (never NaN, so masked
+  // keys stay inert in the PV product).
+  const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
+  const int st_k = grp_base + (lane >> 4) * kKStride + (lane & 15) * 16;
+  const int st_v = grp_base + kKTileBytes + (lane >> 4) * kVStride + (lane & 15) * 16;
+  uint4 rk[S::kStageBlocks][4], rv[S::kStageBlocks][4];
+  // Block ids of the blocks this wave stages, held in VGPRs so a fetch needs
+  // no dependent scalar load: lane j of ids[i] holds the (clamped) id of
+  // block wave + i W of local tile 64 chunk + j, or 0 past the context.
+  int ids[S::kStageBlocks];
+  int ids_chunk = -1;
+  auto load_ids = [&](int chunk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < S::kStageBlocks; ++i) {
+      const int bl = wave + i * S::W;
+      const int lt = 64 * chunk + lane;
+      const int gb = 4 * (t_first + lt) + bl;
+      int v = 0;
+      if (bl < 4 && lt < t_end - t_first && gb < nblk_seq) v = min(max(bt[gb], 0), p.num_blocks - 1);
+      ids[i] = v;
+    }
+    ids_chunk = chunk;
+  };
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+    const int lt = t - t_first;
+    if ((lt >> 6) != ids_chunk) load_ids(lt >> 6);
+#pragma unroll
+    for (int i = 0; i < S::kStageBlocks; ++i) {
+      const int bl = wave + i * S::W;
+      if (bl < 4) {
+        const int gb = 4 * t + bl;  // block index within the sequence
+        const bool ok = gb < nblk_seq;
+        const int blk = __builtin_amdgcn_readlane(ids[i], lt & 63);
+        const int rows = ok ? min(kBlockSize, L - gb * kBlockSize) : 0;
+        const size_t o = static_cast<size_t>(blk) * blk_stride;
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(kg + o), static_cast<short>(0), rows * kRowBytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(vg + o), static_cast<short>(0), rows * kRowBytes, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kr, lane * 16 + 1024 * j, 0, 0);
+          const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(vr, lane * 16 + 1024 * j, 0, 0);
+          rk[i][j] = make_uint4(a[0], a[1], a[2], a[3]);
+          rv[i][j] = make_uint4(c[0], c[1], c[2], c[3]);
+        }
+      }
+    }
+  };
+  // the staged tile goes to LDS buffer `buf` (tile j of the group: buffer j % 2)
+  auto stash = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+    for (int i = 0; i < S::kStageBlocks; ++i) {
+      const int bl = wave + i * S::W;
+      if (bl < 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 16 * bl + 4 * j;
+          *reinterpret_cast<uint4*>(&lds[st_k + buf * kBufBytes + row * kKStride]) = rk[i][j];
+          *reinterpret_cast<uint4*>(&lds[st_v + buf * kBufBytes + row * kVStride]) = rv[i][j];
+        }
+      }
+    }
+  };
+
+  // per-lane LDS read bases; everything else is a compile-time offset
+  // K rows for S^T: key 32 blk + col, dims 16 kk + 8 half
+  const int k_rd = grp_base + col * kKStride + half * 16;
+  // transposed V reads: k-slots of step (blk, tau) are keys 32 blk + 16 tau +
+  // {0-3, 8-11, 4-7, 12-15}; 16-lane group gq holds slots 8 (gq / 2) .. + 7 of
+  // dims 16 (gq % 2) .. + 15 of each 32-dim block d; source lane src points at
+  // row key0 + src / 4, dims + 4 (src % 4)
+  const int gq = lane >> 4, src = lane & 15;
+  const int v_rd = grp_base + kKTileBytes + (4 * (gq >> 1) + (src >> 2)) * kVStride + 32 * (gq & 1) + 8 * (src & 3);
+
+  f32x16_t o_acc[4];  // O^T, dim block d: lane holds query col, dims 32 d + 8 (i / 4) + 4 half + i % 4
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o_acc[d][i] = 0.f;
+  float m = kEmptyMax, lsum = 0.f;
+  const float sc = p.scale_log2;  // > 0
+
+  f32x16_t s[2];      // S^T of the current tile: keys 32 blk + 8 (i / 4) + 4 half + i % 4, query col
+  bf16x8_t pb[2][2];  // P^T of the previous tile, k-step (blk, tau): S^T entries 8 tau .. 8 tau + 7
+
+  // S^T = K Q^T for the tile in LDS buffer `buf`
+  auto qk = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    f32x16_t acc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) acc[blk][i2] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(&lds[k_rd + buf * kBufBytes + blk * 32 * kKStride + kk * 32]);
+        acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qb[kk], acc[blk], 0, 0, 0);
+      }
+    s[0] = acc[0];
+    s[1] = acc[1];
+  };
+
+  // O^T += V^T P^T for the tile in LDS buffer `buf`
+  auto pv = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int o = v_rd + buf * kBufBytes + (32 * blk + 16 * tau) * kVStride + 64 * d;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(&lds[o]));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(&lds[o + 8 * kVStride]));
+          // move whole dwords: element-wise 16-bit extraction here is lowered
+          // into half-word shuffles that drop the upper dword of each read
+          const uint2 l2 = __builtin_bit_cast(uint2, lo);
+          const uint2 h2 = __builtin_bit_cast(uint2, hi);
+          const bf16x8_t va = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+          o_acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][tau], o_acc[d], 0, 0, 0);
+        }
+      }
+  };
+
+  // causal mask, running max and P = 2^(S sc - m) for absolute tile t
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    float mx = -INFINITY;
+    if (t >= n_plain) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) {
+          const int key = t * kKeysPerTile + 32 * blk + 8 * (i2 / 4) + 4 * half + (i2 % 4);
+          if (key > pos || !q_valid) s[blk][i2] = -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, s[blk][i2]);
+    mx *= sc;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    if (__any(mx > m + kRescaleSlack)) {
+      if (mx > m + kRescaleSlack) {
+        const float a = fast_exp2(m - mx);
+        m = mx;
+        lsum *= a;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int i2 = 0; i2 < 16; ++i2) o_acc[d][i2] *= a;
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          e[j] = fast_exp2(fmaf(s[blk][8 * tau + j], sc, -m));
+          lsum += e[j];
+        }
+        uint4 w;
+        w.x = pack_bf16x2(e[0], e[1]);
+        w.y = pack_bf16x2(e[2], e[3]);
+        w.z = pack_bf16x2(e[4], e[5]);
+        w.w = pack_bf16x2(e[6], e[7]);
+        pb[blk][tau] = as_bf16x8(w);
+      }
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const int n_g = t_end - t_first;  // this group's tiles
+
+  // MFMA phase of local tile i (LDS buffer bufc): S^T of tile i and, when
+  // pvc, O^T += V^T P^T of tile i - 1 (the other buffer).  One basic block;
+  // the scheduling groups keep six MFMA operands in flight from LDS so the
+  // read latency hides behind the MFMAs (16 K reads of 16 bytes for S^T, then
+  // two 8-byte transposed V reads per PV MFMA).
+  auto mphase = [&](auto bufc, auto pvc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    using Other = std::integral_constant<int, 1 - buf>;
+    qk(bufc);
+    if constexpr (decltype(pvc)::value) {
+      pv(Other{});
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int j = 0; j < 10; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 6; ++j) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+
+  // One local tile i (LDS buffer i % 2 == bufc): MFMA phase, barrier,
+  // VALU/memory phase, barrier.  The O rescale in the softmax sees O with
+  // tile i - 1 already accumulated, as the online softmax requires.
+  auto step = [&](auto bufc, auto pvc, int i) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
+    using Other = std::integral_constant<int, 1 - buf>;
+    mphase(bufc, pvc);
+    __syncthreads();
+    // tile i + 1 (loaded during the previous phases) goes to buffer `Other`,
+    // last read by this MFMA phase's PV, which every wave finished before the
+    // barrier above; then the staging registers take tile i + 2's loads
+    if (i + 1 < n_g) stash(Other{});
+    if (i + 2 < n_g) fetch(t_first + i + 2);
+    softmax(t_first + i);
+    __syncthreads();
+  };
+
+  if (S::KS == 2 && grp == 1) __syncthreads();  // run one phase behind group 0
+  if (n_g > 0) {
+    fetch(t_first);
+    stash(B0{});
+  }
+  if (n_g > 1) fetch(t_first + 1);
+  __syncthreads();
+  if (n_g > 0) step(B0{}, std::false_type{}, 0);  // the first tile has no PV of a previous one
+  int i = 1;
+  for (; i + 1 < n_g; i += 2) {
+    step(B1{}, std::true_type{}, i);
+    step(B0{}, std::true_type{}, i + 1);
+  }
+  if (i < n_g) step(B1{}, std::true_type{}, i);
+  // the last tile's PV
+  if (n_g > 0) {
+    if ((n_g - 1) & 1)
+      pv(B1{});
+    else
+      pv(B0{});
+  }
+  if (S::KS == 2 && grp == 0) __syncthreads();
+  // equal barrier counts: group 1 may have one tile fewer than group 0
+  for (int k = 2 * n_g; k < 2 * nA; ++k) __syncthreads();
+
+  // combine the two lane halves of each query's sum
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (S::KS == 2) {
+    // group 1 hands (m, lsum, O^T) to group 0 through LDS (tiles are done)
+    float* xs = reinterpret_cast<float*>(lds) + (wave * 64 + lane) * 66;
+    if (grp == 1) {
+      xs[0] = m;
+      xs[1] = lsum;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) xs[2 + 16 * d + i2] = o_acc[d][i2];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xs[0], l1 = xs[1];
+    const float M = fmaxf(m, m1);
+    const float f0 = fast_exp2(m - M), f1 = fast_exp2(m1 - M);
+    lsum = lsum * f0 + l1 * f1;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) o_acc[d][i2] = o_acc[d][i2] * f0 + xs[2 + 16 * d + i2] * f1;
+    m = M;
+  }
+
+  if (!q_valid) return;
+  const bool empty = !(lsum > 0.f);
+  const float inv = empty ? 0.f : 1.f / lsum;
+  const size_t row = static_cast<size_t>(q0 + qi) * p.Hq + head;
+  uint16_t* orow = p.out + row * kHeadDim;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int dim = 32 * d + 8 * r4 + 4 * half;
+      uint2 w;
+      w.x = pack_bf16x2(o_acc[d][4 * r4] * inv, o_acc[d][4 * r4 + 1] * inv);
+      w.y = pack_bf16x2(o_acc[d][4 * r4 + 2] * inv, o_acc[d][4 * r4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + dim) = w;
+    }
+  if (half == 0 && p.lse) p.lse[row] = empty ? -INFINITY : (m + log2f(lsum)) * kLn2;
+}
+
+// Kernel parameters of a prefill launch (host side).
+inline PrefillParams make_prefill_params(const PrefillArgs& a) {
+  PrefillParams prm{};
+  prm.q = static_cast<const uint16_t*>(a.q);
+  prm.query_start_loc = a.query_start_loc;
+  prm.k_cache = static_cast<const uint16_t*>(a.k_cache);
+  prm.v_cache = static_cast<const uint16_t*>(a.v_cache);
+  prm.block_tables = a.block_tables;
+  prm.context_lens = a.context_lens;
+  prm.out = static_cast<uint16_t*>(a.out);
+  prm.lse = a.lse;
+  prm.max_blocks = a.max_blocks_per_seq;
+  prm.B = a.B;
+  prm.total_q = a.total_q;
+  prm.max_q_len = a.max_q_len;
+  prm.Hq = a.Hq;
+  prm.Hkv = a.Hkv;
+  prm.num_blocks = a.num_blocks;
+  const long cap_bt = static_cast<long>(a.max_blocks_per_seq) * kBlockSize;
+  prm.ctx_cap = static_cast<int>(a.max_context_len < cap_bt ? a.max_context_len : cap_bt);
+  prm.scale_log2 = fabsf(a.scale) * kLog2e;
+  prm.negate_q = a.scale < 0.f;
+  return prm;
+}
+
+}  // namespace pre
+}  // namespace fe

@@ -54,7 +54,7 @@ class Spec:
     """Shape recipe of one workload."""
 
     name: str
-    kind: str  # "decode" or "prefill"
+    kind: str  # "decode", "prefill" or "mixed"
     B: int
     Hq: int
     Hkv: int
@@ -66,6 +66,11 @@ class Spec:
     spike_frac: float = 0.0  # fraction of token positions whose K is x spike_mul
     spike_mul: float = 3.0
     chunk: int = 0  # prefill query chunk per sequence (bottom-right causal)
+    # "mixed": sequences [0, num_decode) are decode rows (1 token appended, 1
+    # query row, lengths drawn from [len_lo, len_hi]); the others are prefill
+    # chunks of `chunk` rows (`append` tokens appended) with length pre_len.
+    num_decode: int = 0
+    pre_len: int = 0
 
 
 # The five workloads.  Names state the model shape and the sizes.
@@ -89,6 +94,12 @@ SPECS = {
     "qwen3_4b_b4_prefix4096_chunk256": Spec("qwen3_4b_b4_prefix4096_chunk256", "prefill", 4, 32, 8, 4352,
                                             4352, append=256, chunk=256),
 }
+# A mixed step of a token-budgeted batcher (decode rows and prefill chunks in
+# one launch): 60 decode rows over 1024..8192 tokens and 4 chunks of 256 new
+# tokens after 4096 cached ones, at the Qwen3-4B layer shape.
+SPECS["qwen3_4b_mixed_dec60_ctx1024-8192_pre4_prefix4096_chunk256"] = Spec(
+    "qwen3_4b_mixed_dec60_ctx1024-8192_pre4_prefix4096_chunk256", "mixed", 64, 32, 8, 1024, 8192, append=256,
+    chunk=256, num_decode=60, pre_len=4352)
 ORDER = list(SPECS)  # default seed of SPECS[ORDER[i]] is i + 1
 
 
@@ -160,11 +171,14 @@ def build(spec: Spec, seed: int, poison: str = "large", keep_contiguous: bool = 
             lens_t = torch.full((B,), spec.len_lo, dtype=torch.int64)
         else:
             lens_t = torch.randint(spec.len_lo, spec.len_hi + 1, (B,), generator=_gen(seed, _LEN))
+        if spec.kind == "mixed":
+            lens_t[spec.num_decode:] = spec.pre_len
     else:
         lens_t = torch.tensor(list(lens), dtype=torch.int64)
         assert lens_t.numel() == B
     lens_l = [int(x) for x in lens_t.tolist()]
-    append = spec.append
+    nd = spec.num_decode if spec.kind == "mixed" else 0
+    appends = [1 if b < nd else spec.append for b in range(B)]
     nblk = [(L + BS - 1) // BS for L in lens_l]
     need = sum(nblk)
     if spec.pool_blocks is not None:
@@ -189,7 +203,7 @@ def build(spec: Spec, seed: int, poison: str = "large", keep_contiguous: bool = 
     tok_off = tok_t % BS
     is_new = torch.zeros(tok_t.shape, dtype=torch.bool)
     for b in range(B):
-        a = min(append, lens_l[b])
+        a = min(appends[b], lens_l[b])
         if a:
             start = sum(lens_l[:b])
             is_new[start + lens_l[b] - a : start + lens_l[b]] = True
@@ -197,8 +211,8 @@ def build(spec: Spec, seed: int, poison: str = "large", keep_contiguous: bool = 
 
     qsl = None
     total_q = B
-    if spec.kind == "prefill":
-        chunks = [min(spec.chunk, L) for L in lens_l]
+    if spec.kind in ("prefill", "mixed"):
+        chunks = [1 if b < nd else min(spec.chunk, L) for b, L in enumerate(lens_l)]
         qsl = torch.tensor([0] + list(np.cumsum(chunks)), dtype=torch.int32)
         total_q = int(qsl[-1])
 
@@ -241,10 +255,13 @@ def make(name: str, seed: Optional[int] = None, **kw) -> Workload:
 
 
 def custom(kind: str, B: int, Hq: int, Hkv: int, lens, seed: int, append: int = 0, chunk: int = 0,
-           spike_frac: float = 0.0, pool_blocks: Optional[int] = None, layers: int = 1, **kw) -> Workload:
-    """Ad-hoc workload with explicit lengths (edge cases, small parity sizes)."""
+           spike_frac: float = 0.0, pool_blocks: Optional[int] = None, layers: int = 1, num_decode: int = 0,
+           **kw) -> Workload:
+    """Ad-hoc workload with explicit lengths (edge cases, small parity sizes).
+    For kind "mixed", lens lists every sequence; the first num_decode are
+    decode rows."""
     lens = list(lens)
     spec = Spec(f"custom_{kind}_b{B}_h{Hq}x{Hkv}", kind, B, Hq, Hkv, min(lens) if lens else 0,
                 max(lens) if lens else 0, append=append, layers=layers, pool_blocks=pool_blocks,
-                spike_frac=spike_frac, chunk=chunk)
+                spike_frac=spike_frac, chunk=chunk, num_decode=num_decode)
     return build(spec, seed, lens=lens, **kw)

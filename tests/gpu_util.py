@@ -91,3 +91,18 @@ class DeviceWorkload:
                                       w.max_context_len, w.scale)
         torch.cuda.synchronize()
         return out, lse
+
+    def mixed(self, num_partitions=0, workspace=None):
+        """Decode rows (the first spec.num_decode sequences) and prefill chunks in one launch."""
+        w = self.w
+        nd = w.spec.num_decode
+        total_q = self.q.shape[0]
+        out = torch.full((total_q, w.Hq, 128), float("nan"), dtype=torch.bfloat16, device=self.dev)
+        lse = torch.full((total_q, w.Hq), float("nan"), dtype=torch.float32, device=self.dev)
+        qsl = w.query_start_loc.tolist()
+        chunks = [b - a for a, b in zip(qsl[:-1], qsl[1:])]
+        mql = max(chunks[nd:], default=0)
+        fe.fe_paged_gqa_mixed(out, lse, self.q, self.qsl, self.kc, self.vc, self.bt, self.lens, nd, mql,
+                              w.max_context_len, w.scale, num_partitions=num_partitions, workspace=workspace)
+        torch.cuda.synchronize()
+        return out, lse

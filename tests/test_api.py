@@ -157,3 +157,45 @@ def test_binding_refuses_host_tensors(lib):
     with pytest.raises(ValueError, match="device tensor"):
         fe.fe_paged_gqa_decode(torch.empty_like(q), None, q, kc, kc, torch.zeros(1, 4, dtype=torch.int32),
                                torch.ones(1, dtype=torch.int32), 16, 0.088, num_partitions=1)
+
+
+def mix(lib, **kw):
+    a = dict(out=P, lse=None, q=P, qsl=P, k=P, v=P, bt=P, mb=8, cl=P, B=3, nd=2, tq=18, mql=16, Hq=32, Hkv=8, D=128,
+             BS=16, NB=64, mcl=128, scale=0.088, parts=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.fe_paged_gqa_mixed(a["out"], a["lse"], a["q"], a["qsl"], a["k"], a["v"], a["bt"], a["mb"], a["cl"],
+                                  a["B"], a["nd"], a["tq"], a["mql"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["NB"],
+                                  a["mcl"], a["scale"], a["parts"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_mixed_argument_errors(lib):
+    assert mix(lib, qsl=None) == NULL
+    assert mix(lib, out=None) == NULL
+    assert mix(lib, nd=-1) == INVALID
+    assert mix(lib, nd=4) == INVALID  # more decode rows than sequences
+    assert mix(lib, nd=3, tq=2) == INVALID  # fewer query rows than decode rows
+    assert mix(lib, Hq=12) == INVALID
+    assert mix(lib, parts=-1) == INVALID
+    assert mix(lib, scale=float("inf")) == INVALID
+    assert mix(lib, D=64) == UNSUPPORTED
+    assert mix(lib, Hq=72) == UNSUPPORTED
+    need = lib.fe_paged_gqa_mixed_workspace_size(2, 32, 8, 128, 4096, 4)
+    assert need > 0
+    assert mix(lib, mcl=4096, mb=256, parts=4) == WORKSPACE
+    assert mix(lib, mcl=4096, mb=256, parts=4, ws=P, wsb=need - 1) == WORKSPACE
+    assert "workspace" in fe.fe_last_error()
+    assert mix(lib, B=0, nd=0) == OK
+    assert mix(lib, tq=0, nd=0) == OK
+
+
+def test_mixed_workspace_plan(lib):
+    ws = lib.fe_paged_gqa_mixed_workspace_size
+    assert ws(0, 32, 8, 128, 8192, 0) == 0          # no decode rows: nothing to split
+    assert ws(4, 32, 8, 128, 1024, 0) == 0          # 64 blocks: one automatic partition
+    # 8192 tokens = 512 blocks: automatic ranges of 64 blocks -> 8 partitions;
+    # counters + fp32 partials + their LSEs
+    need = ws(4, 32, 8, 128, 8192, 0)
+    assert need >= 4 * 8 * 4 + 4 * 32 * 8 * (128 + 1) * 4
+    assert ws(4, 32, 8, 128, 4096, 1) == 0          # one range of 256 blocks
+    assert ws(4, 32, 8, 128, 8192, 1) > 0           # a range holds at most 256 blocks: raised to 2
+    assert ws(4, 30, 8, 128, 8192, 0) == ctypes.c_size_t(-1).value
