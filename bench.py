@@ -109,12 +109,21 @@ def time_separate_calls(fe, torch, w, x, nd, qsl, bt, lens, mcl, steps, stream) 
     return a.elapsed_time(b) / steps
 
 
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "decode_body.h", "fe_device.h"],
+    "prefill": ["prefill.hip", "prefill_body.h", "fe_device.h"],
+    "mixed": ["mixed.hip", "decode_body.h", "prefill_body.h", "fe_device.h"],
+}
+
+
 def kernel_source_digest(kind: str) -> str:
-    """Digest of the source file of the timed kernel (traffic counters are
+    """Digest of the source files of the timed kernel (traffic counters are
     only reported while they were taken on this exact source)."""
-    name = "decode.hip" if kind == "decode" else "prefill.hip"
-    with open(os.path.join(ROOT, "paged_kv_gqa_slot_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "paged_kv_gqa_slot_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kind: str, num_partitions: int):
@@ -129,7 +138,7 @@ def measured_traffic(workload: str, kind: str, num_partitions: int):
         return None
     if not rec or rec.get("source_sha256_16") != kernel_source_digest(kind):
         return None
-    if kind == "decode" and rec.get("num_partitions") != num_partitions:
+    if kind in ("decode", "mixed") and rec.get("num_partitions") != num_partitions:
         return None
     return rec.get("bytes_per_launch")
 
@@ -320,7 +329,7 @@ def main():
         bound_us = max(t_hbm, t_mfma)
         value = ms_per_step * 1e3
         roof = {"bound": "hbm+mfma", "achieved": round(att_avg_ms * 1e3, 2), "peak": round(bound_us, 2), "unit": "us",
-                "frac": round(bound_us / (att_avg_ms * 1e3), 4), "traffic": None,
+                "frac": round(bound_us / (att_avg_ms * 1e3), 4), "traffic": measured_traffic(spec.name, "mixed", P),
                 "kernel": "fe_paged_gqa_mixed (gqa_mixed_kernel)", "decode_rows_bytes": dec_bytes,
                 "prefill_flops": flops, "hbm_bound_us": round(t_hbm, 2), "mfma_bound_us": round(t_mfma, 2),
                 "separate_calls_us": round(sep_us, 2), "avg_ms": round(att_avg_ms, 5),
