@@ -198,6 +198,80 @@ def cpu_baseline(w, budget_s: float):
                       f"({el:.1f} s); flops counted for those rows"}
 
 
+def norm_rope_bytes(T: int, Hq: int, Hkv: int) -> int:
+    """Algorithmic HBM bytes of one fused norm/rotary/append call: read q, k,
+    v and each token's table row (fp32, 128 entries) plus its position and
+    slot; write q_out and the k and v rows into the pools.  The two norm
+    weight vectors (512 B) are left out."""
+    row = 128 * 2
+    return T * ((Hq + 2 * Hkv) * row + 128 * 4 + 8) + T * (Hq + 2 * Hkv) * row
+
+
+def bench_norm_rope(args, w, fe, inputs, torch, dev):
+    """The fused per-head QK-RMSNorm + rotary + append step over workload w's
+    appended tokens (one call per step)."""
+    c = inputs.norm_rope_case(w, w.seed)
+    T = int(c.positions.numel())
+    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+    qw, kw, cs = c.q_norm_w.to(dev), c.k_norm_w.to(dev), c.cos_sin.to(dev)
+    pos, sm = c.positions.to(dev), c.slot_mapping.to(dev)
+    kc, vc = c.k_cache.to(dev), c.v_cache.to(dev)
+    q_out = torch.empty_like(q)
+
+    def step():
+        fe.fe_qk_norm_rope_append(q_out, q, k, v, qw, kw, cs, pos, sm, kc, vc, c.eps)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    avg = sum(per) / len(per)
+    nbytes = norm_rope_bytes(T, w.Hq, w.Hkv)
+    achieved = nbytes / (avg * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "fe_qk_norm_rope_append (qk_norm_rope_kernel)", "per_launch_bytes": nbytes,
+            "avg_ms": round(avg, 5), "median_ms": round(per[len(per) // 2], 5)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = os.cpu_count() or 1
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.qk_norm_rope_append(c.q, c.k, c.v, c.q_norm_w, c.k_norm_w, c.cos_sin, c.positions,
+                                       c.slot_mapping, c.k_cache, c.v_cache, c.eps)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_budget, 10.0) or reps >= 20:
+                break
+        cpu = {"value": round(nbytes / (el / reps) / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"fp64 oracle over all {T} tokens (norm/rotary on {threads} threads, append single-threaded), "
+                         f"{reps} repetitions, {el / reps * 1e3:.1f} ms each"}
+    cfg = {"workload": f"norm_rope:{w.spec.name}", "tokens": T, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": 128,
+           "block_size": 16, "table_rows": int(c.cos_sin.shape[0]), "seed": w.seed}
+    rec = {"metric": "fused QK-RMSNorm + rotary + KV append, achieved HBM GB/s, Qwen3-4B shape",
+           "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg, "roofline": roof,
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +282,8 @@ def main():
     ap.add_argument("--partitions", type=int, default=0, help="decode split-K factor (0 = automatic)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=["attention", "norm_rope"], default="attention",
+                    help="norm_rope: time the fused QK-RMSNorm + rotary + append step on the workload's new tokens")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (rocprofv3 counter calibration)")
     args = ap.parse_args()
@@ -228,6 +304,9 @@ def main():
     w = inputs.make(args.workload, seed=args.seed)
     spec = w.spec
     log(f"  B={w.B} Hq={w.Hq} Hkv={w.Hkv} layers={len(w.layers)} kv_tokens={w.kv_tokens} pool={w.num_blocks} blocks")
+
+    if args.op == "norm_rope":
+        return bench_norm_rope(args, w, fe, inputs, torch, dev)
 
     L = [dict(kc=l.k_cache.to(dev), vc=l.v_cache.to(dev), q=l.q.to(dev), kn=l.k_new.to(dev), vn=l.v_new.to(dev))
          for l in w.layers]

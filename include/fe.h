@@ -36,6 +36,8 @@
  *     independent.
  *   - Every call is asynchronous on `stream` (0 = the null stream).  One
  *     stream orders an append before the attention that reads it.
+ *   - Tensor pointers must be 16-byte aligned (FE_ERR_INVALID_ARG otherwise);
+ *     the kernels move 16-byte units.
  *   - Return value: FE_OK (0), or a negative fe_status.  Argument errors are
  *     detected on the host before anything is enqueued, so outputs are
  *     untouched on error.  A failed launch returns FE_ERR_HIP.
@@ -209,6 +211,39 @@ int fe_paged_gqa_mixed(void* out, float* lse, const void* q, const int32_t* quer
                        const int32_t* context_lens, int B, int num_decode, int total_q, int max_q_len, int Hq,
                        int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale, int num_partitions,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Fused per-head QK-RMSNorm + rotary embedding + KV append: the step just
+ * before attention, done in one pass so the normed and rotated k does not
+ * make a round trip through HBM before it is appended.
+ *   For every token i in [0, T), in fp32, rounded once to bf16 (nearest even):
+ *     each q head row x = q[i][h] and k head row x = k[i][g]:
+ *       y = x * w / sqrt(mean_d(x[d]^2) + eps)   (w = q_norm_w or k_norm_w)
+ *       with p = positions[i] clamped into [0, max_pos), for d < D/2:
+ *         c = cos_sin[p][d], s = cos_sin[p][D/2 + d]
+ *         out[d] = y[d] c - y[D/2 + d] s,  out[D/2 + d] = y[D/2 + d] c + y[d] s
+ *     q_out[i][h] = out of q head h;
+ *     with s = slot_mapping[i] in [0, num_blocks * BS): the cache slot s of KV
+ *     head g gets out of k head g (k_cache) and v[i][g] bit for bit (v_cache);
+ *     other slots are skipped (q_out is still written).
+ *   q, q_out       bf16 [T][Hq][D]; q_out may be q itself (in place)
+ *   k, v           bf16 [T][Hkv][D]
+ *   q_norm_w, k_norm_w  bf16 [D]
+ *   cos_sin        fp32 [max_pos][D]: the cosines of the D/2 angles of a
+ *                  position, then their sines (the caller's rotary table)
+ *   positions      int32 [T]
+ *   slot_mapping, k_cache, v_cache: as in fe_paged_kv_append
+ *   eps            finite, >= 0
+ *   All tensor pointers 16-byte aligned.  T == 0 is a no-op.
+ * Source: "Make the Engine Talk" section 1.3 (RMSNorm and rotary position
+ * embeddings among the forward pass's mechanisms); ForgeEngine README, "What
+ * it implements" (RMSNorm kernel, paged KV cache).  The formulas are this
+ * library's reading: the pages name the mechanisms only.
+ */
+int fe_qk_norm_rope_append(void* q_out, const void* q, const void* k, const void* v, const void* q_norm_w,
+                           const void* k_norm_w, const float* cos_sin, int max_pos, const int32_t* positions,
+                           const int32_t* slot_mapping, void* k_cache, void* v_cache, int T, int Hq, int Hkv, int D,
+                           int BS, int num_blocks, float eps, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* fe_status_string(int status);

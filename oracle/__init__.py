@@ -67,6 +67,10 @@ def _load():
     lib.oracle_merge.restype = None
     lib.oracle_prefill_chunk.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, Dd, P, I, I]
     lib.oracle_prefill_chunk.restype = I
+    lib.oracle_qk_norm_rope.argtypes = [P, P, P, P, I, P, I, I, I, Dd, I]
+    lib.oracle_qk_norm_rope.restype = I
+    lib.oracle_narrow_bf16.argtypes = [Dd]
+    lib.oracle_narrow_bf16.restype = ctypes.c_uint16
     _lib = lib
     return lib
 
@@ -178,3 +182,37 @@ def prefill_chunk(q, query_start_loc, k_cache, v_cache, block_tables, context_le
     if rc:
         raise ValueError(f"oracle_prefill_chunk rejected the shapes (status {rc})")
     return out, lse
+
+
+def _f32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def norm_rope(x, w, cos_sin, positions, eps, nthreads=None):
+    """Per-head RMSNorm + rotary embedding of x [T][H][D] (bf16).  Returns the
+    bf16 result as uint16 bits [T][H][D]."""
+    xb, wb, cs, pos = _bits(x), _bits(w), _f32(cos_sin), _i32(positions)
+    T, H, D = xb.shape
+    assert wb.shape == (D,) and cs.ndim == 2 and cs.shape[1] == D and pos.shape == (T,)
+    out = np.zeros((T, H, D), np.uint16)
+    rc = _load().oracle_qk_norm_rope(_ptr(out), _ptr(xb), _ptr(wb), _ptr(cs), cs.shape[0], _ptr(pos), T, H, D,
+                                     float(eps), _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_qk_norm_rope rejected the arguments (status {rc})")
+    return out
+
+
+def qk_norm_rope_append(q, k, v, q_norm_w, k_norm_w, cos_sin, positions, slot_mapping, k_cache, v_cache, eps):
+    """The fused step: normed + rotated q (bits [T][Hq][D]), and the pools after
+    appending normed + rotated k and the unchanged v at the slots."""
+    q_out = norm_rope(q, q_norm_w, cos_sin, positions, eps)
+    k_rows = norm_rope(k, k_norm_w, cos_sin, positions, eps)
+    kc, vc = append(k_rows, v, slot_mapping, k_cache, v_cache)
+    return q_out, k_rows, kc, vc
+
+
+def narrow_bf16(v: float) -> int:
+    """Nearest-even bf16 bits of a double (the oracle's own rounding)."""
+    return int(_load().oracle_narrow_bf16(float(v)))

@@ -26,9 +26,27 @@
 //     position L - C + i and sees keys 0 .. L - C + i (bottom-right causal);
 //   * L = 0 gives out = 0 and lse = -inf.
 //
+// The step before attention (the NEXT row after it): "Make the Engine Talk"
+// section 1.3 names RMSNorm and rotary position embeddings among the forward
+// pass's mechanisms, and the ForgeEngine README's "What it implements" table
+// lists an RMSNorm kernel.  The pages give no formula; the readings here are
+// per-head RMSNorm y = x w / sqrt(mean_d x^2 + eps) of each q and k head row
+// (one weight vector of D entries for q, one for k), then the rotate-half
+// rotary embedding: dims d and d + D/2 (d < D/2) turn by the angle whose
+// cosine and sine the caller's table holds at [position][d] and
+// [position][D/2 + d]; the result is rounded once to bf16 (nearest even).
+//
 // Arithmetic: every bf16 value widens exactly to double; scale is the caller's
 // value; dot products sum in increasing d, softmax sums in increasing t; the
 // softmax is the two-pass max-shifted definition.  No blocking or reordering.
+//
+// Parity pins (tests/test_oracle.py) for the norm/rotary step: identity
+// rotation gives unit mean square; a quarter turn and a half turn are exact
+// permutations/negations of the identity result; scaling x by 2 changes
+// nothing and scaling w by 2 doubles the result exactly; heads are
+// independent; a one-hot row matches its closed form (tests/golden); and the
+// bf16 rounding matches torch's float32 -> bfloat16 conversion where the value
+// is a float32.
 //
 // Parity pins (tests/test_oracle.py): brute force on contiguous copies and
 // torch's scaled_dot_product_attention in float64; block-table permutation
@@ -51,6 +69,26 @@ double widen_bf16(uint16_t bits) {
   float f;
   std::memcpy(&f, &u, sizeof f);
   return static_cast<double>(f);
+}
+
+// Nearest-even bf16 of a double, rounded once from the double's value: 8
+// significant bits in the normal range, spacing 2^-133 below it, infinity
+// beyond the largest finite bf16.
+uint16_t narrow_bf16(double v) {
+  if (std::isnan(v)) return 0x7FC0;
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  const double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  std::frexp(a, &e);  // a = m 2^e, 0.5 <= m < 1
+  const int shift = e - 1 >= -126 ? 8 - e : 133;  // units of the last kept bit
+  const double r = std::nearbyint(std::ldexp(a, shift)) ;  // default rounding: nearest even
+  const double q = std::ldexp(r, -shift);
+  if (q >= 0x1p128) return sign | 0x7F80;
+  const float f = static_cast<float>(q);  // exact: at most 8 significant bits
+  uint32_t u;
+  std::memcpy(&u, &f, sizeof u);
+  return static_cast<uint16_t>(sign | ((u >> 16) & 0x7FFF));
 }
 
 struct Cache {
@@ -263,5 +301,40 @@ int oracle_prefill_chunk(double* out, double* lse, const uint16_t* q, const int3
   });
   return 0;
 }
+
+// Per-head RMSNorm and rotary embedding of rows x [T][H][D] (bf16), written
+// as bf16 to out [T][H][D].  w: [D] bf16 norm weights; cos_sin: [max_pos][D]
+// fp32 (cosines of the D/2 angles, then their sines); positions: [T], each
+// clamped into [0, max_pos).  Returns 0, or -1 for odd D or bad sizes.
+int oracle_qk_norm_rope(uint16_t* out, const uint16_t* x, const uint16_t* w, const float* cos_sin, int max_pos,
+                        const int32_t* positions, int T, int H, int D, double eps, int nthreads) {
+  if (T < 0 || H <= 0 || D <= 0 || D % 2 != 0 || max_pos <= 0) return -1;
+  const int half = D / 2;
+  parallel_for(T * H, nthreads, [&](int th) {
+    const int t = th / H;
+    const uint16_t* row = x + static_cast<size_t>(th) * D;
+    double ss = 0.0;
+    for (int d = 0; d < D; ++d) {
+      const double v = widen_bf16(row[d]);
+      ss += v * v;
+    }
+    const double inv_rms = 1.0 / std::sqrt(ss / D + eps);
+    std::vector<double> y(D);
+    for (int d = 0; d < D; ++d) y[d] = widen_bf16(row[d]) * inv_rms * widen_bf16(w[d]);
+    int p = positions[t];
+    p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
+    const float* cs = cos_sin + static_cast<size_t>(p) * D;
+    uint16_t* o = out + static_cast<size_t>(th) * D;
+    for (int d = 0; d < half; ++d) {
+      const double c = cs[d], s = cs[half + d];
+      o[d] = narrow_bf16(y[d] * c - y[half + d] * s);
+      o[half + d] = narrow_bf16(y[half + d] * c + y[d] * s);
+    }
+  });
+  return 0;
+}
+
+// The narrowing used above, exposed for its pin.
+uint16_t oracle_narrow_bf16(double v) { return narrow_bf16(v); }
 
 }  // extern "C"

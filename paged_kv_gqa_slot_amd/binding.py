@@ -54,6 +54,8 @@ def load_library():
     lib.fe_paged_gqa_mixed_workspace_size.restype = Z
     lib.fe_paged_gqa_mixed.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fe_paged_gqa_mixed.restype = I
+    lib.fe_qk_norm_rope_append.argtypes = [P, P, P, P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, F, P]
+    lib.fe_qk_norm_rope_append.restype = I
     lib.fe_status_string.argtypes = [I]
     lib.fe_status_string.restype = ctypes.c_char_p
     lib.fe_last_error.argtypes = []
@@ -189,3 +191,23 @@ def fe_paged_gqa_mixed(out, lse, q, query_start_loc, k_cache, v_cache, block_tab
         int(max_q_len), Hq, Hkv, D, BS, NB, int(max_context_len), float(scale), int(num_partitions), ws_ptr, ws_have,
         _stream(stream))
     _check(rc, "fe_paged_gqa_mixed")
+
+
+def fe_qk_norm_rope_append(q_out, q, k, v, q_norm_w, k_norm_w, cos_sin, positions, slot_mapping, k_cache, v_cache,
+                           eps: float, stream=None) -> None:
+    """Per-head RMSNorm + rotary embedding of q and k, then append of k and v
+    into the pools; q_out may be q (in place)."""
+    T, Hq, D = q.shape
+    NB, Hkv, BS, _ = k_cache.shape
+    if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D) or tuple(q_out.shape) != (T, Hq, D):
+        raise ValueError("q/q_out must be [T][Hq][D] and k/v [T][Hkv][D]")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != D:
+        raise ValueError("cos_sin must be [max_pos][D]")
+    rc = load_library().fe_qk_norm_rope_append(
+        _dev(q_out, torch.bfloat16, "q_out", 3), _dev(q, torch.bfloat16, "q", 3), _dev(k, torch.bfloat16, "k", 3),
+        _dev(v, torch.bfloat16, "v", 3), _dev(q_norm_w, torch.bfloat16, "q_norm_w", 1),
+        _dev(k_norm_w, torch.bfloat16, "k_norm_w", 1), _dev(cos_sin, torch.float32, "cos_sin", 2), cos_sin.shape[0],
+        _dev(positions, torch.int32, "positions", 1), _dev(slot_mapping, torch.int32, "slot_mapping", 1),
+        _dev(k_cache, torch.bfloat16, "k_cache", 4), _dev(v_cache, torch.bfloat16, "v_cache", 4), T, Hq, Hkv, D, BS,
+        NB, float(eps), _stream(stream))
+    _check(rc, "fe_qk_norm_rope_append")

@@ -5,6 +5,7 @@
 
 #include <math.h>
 
+#include <cstdint>
 #include <cstdio>
 #include <string>
 
@@ -39,6 +40,9 @@ int check_heads(const char* func, int Hq, int Hkv, int D, int BS) {
   return FE_OK;
 }
 
+// The kernels move 16-byte units; every tensor pointer must allow that.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -69,6 +73,8 @@ int fe_paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot
     if (!k_cache || !v_cache) return fail(FE_ERR_NULL, fn, "k_cache and v_cache must not be NULL");
     if (T == 0) return FE_OK;
     if (!k_new || !v_new || !slot_mapping) return fail(FE_ERR_NULL, fn, "k_new, v_new, slot_mapping must not be NULL");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+      return fail(FE_ERR_INVALID_ARG, fn, "k_new, v_new, k_cache, v_cache must be 16-byte aligned");
     const hipError_t e = fe::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, T, num_blocks, Hkv, stream);
     return e == hipSuccess ? FE_OK : hip_fail(e, fn);
   } catch (...) {
@@ -103,6 +109,8 @@ int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cach
     if (!isfinite(scale)) return fail(FE_ERR_INVALID_ARG, fn, "scale must be finite");
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
       return fail(FE_ERR_NULL, fn, "out, q, k_cache, v_cache, block_tables, context_lens must not be NULL");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+      return fail(FE_ERR_INVALID_ARG, fn, "out, q, k_cache, v_cache, workspace must be 16-byte aligned");
     fe::DecodePlan plan;
     if (!fe::plan_decode(B, Hq, Hkv, max_context_len, num_partitions, &plan))
       return fail(FE_ERR_INVALID_ARG, fn, "cannot plan these sizes");
@@ -134,6 +142,8 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
     if (!out || !q || !query_start_loc || !k_cache || !v_cache || !block_tables || !context_lens)
       return fail(FE_ERR_NULL, fn,
                   "out, q, query_start_loc, k_cache, v_cache, block_tables, context_lens must not be NULL");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+      return fail(FE_ERR_INVALID_ARG, fn, "out, q, k_cache, v_cache must be 16-byte aligned");
     fe::PrefillArgs a{out, lse, q, query_start_loc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                       B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale};
     const hipError_t e = fe::launch_prefill(a, stream);
@@ -176,10 +186,39 @@ int fe_paged_gqa_mixed(void* out, float* lse, const void* q, const int32_t* quer
     if (!out || !q || !query_start_loc || !k_cache || !v_cache || !block_tables || !context_lens)
       return fail(FE_ERR_NULL, fn,
                   "out, q, query_start_loc, k_cache, v_cache, block_tables, context_lens must not be NULL");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+      return fail(FE_ERR_INVALID_ARG, fn, "out, q, k_cache, v_cache, workspace must be 16-byte aligned");
     fe::MixedArgs a{{out, lse, q, query_start_loc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale},
                     num_decode, plan, workspace};
     const hipError_t e = fe::launch_mixed(a, stream);
+    return e == hipSuccess ? FE_OK : hip_fail(e, fn);
+  } catch (...) {
+    return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
+  }
+}
+
+int fe_qk_norm_rope_append(void* q_out, const void* q, const void* k, const void* v, const void* q_norm_w,
+                           const void* k_norm_w, const float* cos_sin, int max_pos, const int32_t* positions,
+                           const int32_t* slot_mapping, void* k_cache, void* v_cache, int T, int Hq, int Hkv, int D,
+                           int BS, int num_blocks, float eps, hipStream_t stream) {
+  static const char* fn = "fe_qk_norm_rope_append";
+  try {
+    if (T < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || num_blocks <= 0 || max_pos <= 0)
+      return fail(FE_ERR_INVALID_ARG, fn, "T must be >= 0; Hq, Hkv, D, BS, num_blocks, max_pos positive");
+    if (D != fe::kHeadDim) return fail(FE_ERR_UNSUPPORTED, fn, "only head_dim 128 is built");
+    if (BS != fe::kBlockSize) return fail(FE_ERR_UNSUPPORTED, fn, "only KV block size 16 is built");
+    if (!isfinite(eps) || eps < 0.f) return fail(FE_ERR_INVALID_ARG, fn, "eps must be finite and >= 0");
+    if (T == 0) return FE_OK;
+    if (!q_out || !q || !k || !v || !q_norm_w || !k_norm_w || !cos_sin || !positions || !slot_mapping || !k_cache ||
+        !v_cache)
+      return fail(FE_ERR_NULL, fn, "no pointer may be NULL when T > 0");
+    if (!aligned16(q_out) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_norm_w) ||
+        !aligned16(k_norm_w) || !aligned16(cos_sin) || !aligned16(k_cache) || !aligned16(v_cache))
+      return fail(FE_ERR_INVALID_ARG, fn, "q_out, q, k, v, the norm weights, cos_sin and the pools must be 16-byte aligned");
+    const fe::NormRopeArgs a{q_out, q, k, v, q_norm_w, k_norm_w, cos_sin, max_pos, positions, slot_mapping, k_cache,
+                             v_cache, T, Hq, Hkv, num_blocks, eps};
+    const hipError_t e = fe::launch_qk_norm_rope(a, stream);
     return e == hipSuccess ? FE_OK : hip_fail(e, fn);
   } catch (...) {
     return fail(FE_ERR_INTERNAL, fn, "unexpected exception");

@@ -83,10 +83,28 @@ struct MixedArgs {
   void* workspace;
 };
 
+struct NormRopeArgs {
+  void* q_out;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* q_norm_w;
+  const void* k_norm_w;
+  const float* cos_sin;
+  int max_pos;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+  int T, Hq, Hkv, num_blocks;
+  float eps;
+};
+
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_cache,
                             void* v_cache, int T, int num_blocks, int Hkv, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_mixed(const MixedArgs& a, hipStream_t stream);
+hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream);
 
 }  // namespace fe

@@ -1,0 +1,167 @@
+// Fused per-head QK-RMSNorm + rotary embedding + KV append: the step that
+// turns one batch of projected q/k/v rows into the attention inputs ("Make
+// the Engine Talk" section 1.3: RMSNorm and rotary position embeddings are
+// forward-pass mechanisms; ForgeEngine README, "What it implements": an
+// RMSNorm kernel and the paged KV cache).  Doing it in one pass keeps the
+// normed and rotated k from making a round trip through HBM before append.
+//
+// For each head row x (D = 128) of q and k:
+//   y = x * w / sqrt(mean(x^2) + eps)                    (per-head RMSNorm)
+//   rotate-half embedding, d < 64, table row p = positions[t]:
+//     y'[d] = y[d] c_d - y[d + 64] s_d,  y'[d + 64] = y[d + 64] c_d + y[d] s_d
+// in fp32, rounded once to bf16.  q rows go to q_out; k rows and the
+// unchanged v rows go to their cache slot.
+//
+// 16 lanes per 256-byte row, 16 bytes each: lane c holds dims 8c .. 8c + 7.
+// The sum of squares is a DPP reduction over the 16 lanes; the rotation
+// partner of dims 8c .. 8c + 7 is lane c ^ 8 of the same row (DPP row_ror:8).
+#include <math.h>
+
+#include "fe_device.h"
+#include "fe_kernels.h"
+
+namespace fe {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Rows are read and written once: non-temporal 16-byte loads and stores.
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_nt(void* p, uint4 w) {
+  const u32x4_t v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, static_cast<u32x4_t*>(p));
+}
+
+constexpr int kRowLanes = 16;
+constexpr int kThreads = 256;
+constexpr int kRowsPerWg = kThreads / kRowLanes;
+
+struct NormRopeParams {
+  uint16_t* q_out;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* q_w;
+  const uint16_t* k_w;
+  const float* cos_sin;
+  const int32_t* positions;
+  const int32_t* slots;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int T, Hq, Hkv, max_pos;
+  int64_t num_slots;
+  float eps;
+};
+
+// Sum over the 16 lanes of a DPP row; every lane gets it.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppRowMirror>(x);
+  return x;
+}
+
+__global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeParams p) {
+  const int c = threadIdx.x & (kRowLanes - 1);
+  const int64_t R = static_cast<int64_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x / kRowLanes);
+  const int rows_per_tok = p.Hq + 2 * p.Hkv;
+  // Rows past the end still run the row-wide DPP reductions (on zeros) so
+  // that every lane of a row takes the same path; they store nothing.
+  const bool live = R < static_cast<int64_t>(p.T) * rows_per_tok;
+  const int t = live ? static_cast<int>(R / rows_per_tok) : 0;
+  const int r = live ? static_cast<int>(R % rows_per_tok) : 0;
+  const int kind = r < p.Hq ? 0 : (r < p.Hq + p.Hkv ? 1 : 2);  // q, k, v row
+  const int head = kind == 0 ? r : (kind == 1 ? r - p.Hq : r - p.Hq - p.Hkv);
+  const int64_t slot = live ? p.slots[t] : -1;
+  const bool slot_ok = slot >= 0 && slot < p.num_slots;
+
+  const uint16_t* src = kind == 0 ? p.q + (static_cast<size_t>(t) * p.Hq + head) * kHeadDim
+                                  : (kind == 1 ? p.k : p.v) + (static_cast<size_t>(t) * p.Hkv + head) * kHeadDim;
+  const uint4 xw = live ? load_nt(reinterpret_cast<const uint4*>(src) + c) : make_uint4(0, 0, 0, 0);
+  const size_t cache_off =
+      slot_ok ? ((static_cast<size_t>(slot / kBlockSize) * p.Hkv + head) * kBlockSize + slot % kBlockSize) * kHeadDim
+              : 0;
+  if (kind == 2) {  // v: bit copy into the pool
+    if (live && slot_ok) store_nt(reinterpret_cast<uint4*>(p.v_cache + cache_off) + c, xw);
+    return;
+  }
+
+  float x[8];
+  x[0] = bf16_lo(xw.x); x[1] = bf16_hi(xw.x);
+  x[2] = bf16_lo(xw.y); x[3] = bf16_hi(xw.y);
+  x[4] = bf16_lo(xw.z); x[5] = bf16_hi(xw.z);
+  x[6] = bf16_lo(xw.w); x[7] = bf16_hi(xw.w);
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss = fmaf(x[j], x[j], ss);
+  ss = row_sum16(ss);
+  const float inv_rms = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
+
+  const uint4 ww = reinterpret_cast<const uint4*>(kind == 0 ? p.q_w : p.k_w)[c];
+  float y[8];
+  y[0] = x[0] * inv_rms * bf16_lo(ww.x); y[1] = x[1] * inv_rms * bf16_hi(ww.x);
+  y[2] = x[2] * inv_rms * bf16_lo(ww.y); y[3] = x[3] * inv_rms * bf16_hi(ww.y);
+  y[4] = x[4] * inv_rms * bf16_lo(ww.z); y[5] = x[5] * inv_rms * bf16_hi(ww.z);
+  y[6] = x[6] * inv_rms * bf16_lo(ww.w); y[7] = x[7] * inv_rms * bf16_hi(ww.w);
+
+  // the partner dims (d + 64 for lanes 0-7, d - 64 for lanes 8-15)
+  float z[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z[j] = dpp<kDppRowRor8>(y[j]);
+
+  int pos = live ? p.positions[t] : 0;
+  pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);
+  const int d0 = 8 * (c & 7);  // angle index of this lane's first dim
+  const float4* cs = reinterpret_cast<const float4*>(p.cos_sin + static_cast<size_t>(pos) * kHeadDim + d0);
+  const float4 c0 = cs[0], c1 = cs[1];
+  const float4 s0 = cs[16], s1 = cs[17];  // the sines sit 64 floats further
+  const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  // first half: y c - z s; second half: y c + z s
+  const float sgn = c < 8 ? -1.0f : 1.0f;
+  float o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = fmaf(sgn * z[j], sv[j], y[j] * cv[j]);
+  const uint4 ow = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                              pack_bf16x2(o[6], o[7]));
+  if (!live) return;
+  if (kind == 0)
+    store_nt(reinterpret_cast<uint4*>(p.q_out + (static_cast<size_t>(t) * p.Hq + head) * kHeadDim) + c, ow);
+  else if (slot_ok)
+    store_nt(reinterpret_cast<uint4*>(p.k_cache + cache_off) + c, ow);
+}
+
+}  // namespace
+
+hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream) {
+  NormRopeParams p{};
+  p.q_out = static_cast<uint16_t*>(a.q_out);
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.q_w = static_cast<const uint16_t*>(a.q_norm_w);
+  p.k_w = static_cast<const uint16_t*>(a.k_norm_w);
+  p.cos_sin = a.cos_sin;
+  p.positions = a.positions;
+  p.slots = a.slot_mapping;
+  p.k_cache = static_cast<uint16_t*>(a.k_cache);
+  p.v_cache = static_cast<uint16_t*>(a.v_cache);
+  p.T = a.T;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.max_pos = a.max_pos;
+  p.num_slots = static_cast<int64_t>(a.num_blocks) * kBlockSize;
+  p.eps = a.eps;
+  const int64_t rows = static_cast<int64_t>(a.T) * (a.Hq + 2 * a.Hkv);
+  if (rows == 0) return hipSuccess;
+  const unsigned grid = static_cast<unsigned>((rows + kRowsPerWg - 1) / kRowsPerWg);
+  void* args[] = {&p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&qk_norm_rope_kernel), dim3(grid), dim3(kThreads), args, 0,
+                         stream);
+}
+
+}  // namespace fe

@@ -43,6 +43,7 @@ def fp32_scale(head_dim: int = D) -> float:
 # Stream ids: every random quantity gets its own generator so that changing
 # one size does not shift the others.
 _LEN, _PERM, _Q, _K, _V, _SPIKE = 1, 2, 3, 4, 5, 6
+_NR_Q, _NR_K, _NR_V, _NR_W = 7, 8, 9, 10  # inputs of the norm/rotary step
 
 
 def _gen(seed: int, stream: int, layer: int = 0) -> torch.Generator:
@@ -100,6 +101,11 @@ SPECS = {
 SPECS["qwen3_4b_mixed_dec60_ctx1024-8192_pre4_prefix4096_chunk256"] = Spec(
     "qwen3_4b_mixed_dec60_ctx1024-8192_pre4_prefix4096_chunk256", "mixed", 64, 32, 8, 1024, 8192, append=256,
     chunk=256, num_decode=60, pre_len=4352)
+# A larger chunked-prefill step (64 chunks of 256 new tokens after 1024 cached
+# ones, 16384 appended tokens): the token set on which the norm/rotary/append
+# step's streaming rate is measured.
+SPECS["qwen3_4b_b64_prefix1024_chunk256"] = Spec("qwen3_4b_b64_prefix1024_chunk256", "prefill", 64, 32, 8, 1280, 1280,
+                                                 append=256, chunk=256)
 ORDER = list(SPECS)  # default seed of SPECS[ORDER[i]] is i + 1
 
 
@@ -265,3 +271,65 @@ def custom(kind: str, B: int, Hq: int, Hkv: int, lens, seed: int, append: int = 
                 max(lens) if lens else 0, append=append, layers=layers, pool_blocks=pool_blocks,
                 spike_frac=spike_frac, chunk=chunk, num_decode=num_decode)
     return build(spec, seed, lens=lens, **kw)
+
+
+# ----------------------------------------------------------------------------
+# Inputs of the per-head QK-RMSNorm + rotary + append step.
+
+ROPE_BASE = 1_000_000.0  # Qwen3's rotary base
+NORM_EPS = 1e-6          # Qwen3's RMSNorm epsilon
+
+
+def appended_positions(w: Workload) -> torch.Tensor:
+    """Positions of the appended tokens, in slot_mapping order (the last
+    `append` tokens of each sequence; one for a mixed batch's decode rows)."""
+    spec = w.spec
+    nd = spec.num_decode if spec.kind == "mixed" else 0
+    pos = []
+    for b, L in enumerate(w.context_lens.tolist()):
+        a = min(1 if b < nd else spec.append, L)
+        pos.extend(range(L - a, L))
+    return torch.tensor(pos, dtype=torch.int32)
+
+
+def rope_table(max_pos: int, head_dim: int = D, base: float = ROPE_BASE) -> torch.Tensor:
+    """The rotary table a caller keeps, fp32 [max_pos][head_dim]: for position
+    p and pair d < head_dim / 2 the angle p * base^(-2d / head_dim) (in
+    float64), its cosine at [p][d] and its sine at [p][head_dim / 2 + d]."""
+    half = head_dim // 2
+    inv = base ** (-torch.arange(half, dtype=torch.float64) * 2.0 / head_dim)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32).contiguous()
+
+
+@dataclass
+class NormRopeCase:
+    q: torch.Tensor         # bf16 [T][Hq][D], projected, before norm and rotation
+    k: torch.Tensor         # bf16 [T][Hkv][D]
+    v: torch.Tensor         # bf16 [T][Hkv][D]
+    q_norm_w: torch.Tensor  # bf16 [D]
+    k_norm_w: torch.Tensor  # bf16 [D]
+    cos_sin: torch.Tensor   # fp32 [max_pos][D]
+    positions: torch.Tensor  # int32 [T]
+    slot_mapping: torch.Tensor  # int32 [T]
+    k_cache: torch.Tensor   # bf16 pools, before the append
+    v_cache: torch.Tensor
+    eps: float = NORM_EPS
+
+
+def norm_rope_case(w: Workload, seed: int, max_pos: Optional[int] = None) -> NormRopeCase:
+    """The norm/rotary/append step of workload w's appended tokens: fresh
+    projected rows (randn, bf16), norm weights 1 + 0.1 randn (bf16), the
+    workload's slots and pools, and a rotary table covering its positions."""
+    T = int(w.slot_mapping.numel())
+    pos = appended_positions(w)
+    assert pos.numel() == T
+    if max_pos is None:
+        max_pos = int(pos.max().item()) + 1 if T else 1
+    q = torch.randn((T, w.Hq, D), generator=_gen(seed, _NR_Q), dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((T, w.Hkv, D), generator=_gen(seed, _NR_K), dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((T, w.Hkv, D), generator=_gen(seed, _NR_V), dtype=torch.float32).to(torch.bfloat16)
+    ww = 1.0 + 0.1 * torch.randn((2, D), generator=_gen(seed, _NR_W), dtype=torch.float32)
+    return NormRopeCase(q=q, k=k, v=v, q_norm_w=ww[0].to(torch.bfloat16), k_norm_w=ww[1].to(torch.bfloat16),
+                        cos_sin=rope_table(max_pos), positions=pos, slot_mapping=w.slot_mapping.clone(),
+                        k_cache=w.layers[0].k_cache, v_cache=w.layers[0].v_cache)

@@ -199,3 +199,32 @@ def test_mixed_workspace_plan(lib):
     assert ws(4, 32, 8, 128, 4096, 1) == 0          # one range of 256 blocks
     assert ws(4, 32, 8, 128, 8192, 1) > 0           # a range holds at most 256 blocks: raised to 2
     assert ws(4, 30, 8, 128, 8192, 0) == ctypes.c_size_t(-1).value
+
+
+def nr(lib, **kw):
+    a = dict(qo=P, q=P, k=P, v=P, qw=P, kw=P, cs=P, mp=64, pos=P, sm=P, kc=P, vc=P, T=4, Hq=32, Hkv=8, D=128, BS=16,
+             NB=64, eps=1e-6, stream=None)
+    a.update(kw)
+    return lib.fe_qk_norm_rope_append(a["qo"], a["q"], a["k"], a["v"], a["qw"], a["kw"], a["cs"], a["mp"], a["pos"],
+                                      a["sm"], a["kc"], a["vc"], a["T"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["NB"],
+                                      a["eps"], a["stream"])
+
+
+def test_norm_rope_argument_errors(lib):
+    assert nr(lib, cs=None) == NULL
+    assert nr(lib, qo=None) == NULL
+    assert nr(lib, T=-1) == INVALID
+    assert nr(lib, mp=0) == INVALID
+    assert nr(lib, eps=-1.0) == INVALID
+    assert nr(lib, eps=float("nan")) == INVALID
+    assert nr(lib, D=64) == UNSUPPORTED
+    assert nr(lib, BS=32) == UNSUPPORTED
+    assert nr(lib, cs=P + 4) == INVALID and "aligned" in fe.fe_last_error()
+    assert nr(lib, T=0, q=None, k=None, v=None, qo=None) == OK
+
+
+def test_misaligned_pointers_rejected(lib):
+    assert app(lib, kn=P + 2) == INVALID
+    assert dec(lib, q=P + 8) == INVALID
+    assert pre(lib, out=P + 2) == INVALID
+    assert mix(lib, k=P + 4) == INVALID

@@ -284,6 +284,8 @@ def pin_golden_examples():
             continue
         with open(os.path.join(GOLDEN, name)) as f:
             ex = json.load(f)
+        if ex["kind"] not in ("decode", "prefill"):
+            continue
         Hq, Hkv = ex["Hq"], ex["Hkv"]
         ks, vs = [], []
         for seq in ex["sequences"]:
@@ -315,10 +317,120 @@ def pin_golden_examples():
             assert abs(lse[r, h] - val) <= 1e-12 * max(1.0, abs(val)), (name, r, h, lse[r, h], val)
 
 
+# ----------------------------------------------------------------------------
+# the per-head RMSNorm + rotary step (f2): closed forms and invariants
+
+HALF = D // 2
+
+
+def _table(cos_first, sin_second):
+    """One table row: every pair gets the same (cos, sin)."""
+    t = np.zeros((1, D), np.float32)
+    t[0, :HALF] = cos_first
+    t[0, HALF:] = sin_second
+    return t
+
+
+def _nr_inputs(T=5, H=3, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, H, D, generator=g).to(torch.bfloat16)
+    w = (1 + 0.25 * torch.randn(D, generator=g)).to(torch.bfloat16)
+    return x, w
+
+
+def _vals(b):
+    return from_bits(b).double().numpy()
+
+
+def pin_norm_rope_identity_unit_rms():
+    """cos 1, sin 0 and unit weights: each row's mean square is 1 (to bf16 rounding)."""
+    x, _ = _nr_inputs()
+    ones = torch.ones(D, dtype=torch.bfloat16)
+    y = _vals(oracle.norm_rope(x, ones, _table(1.0, 0.0), np.zeros(x.shape[0], np.int32), 0.0))
+    ms = (y ** 2).mean(-1)
+    assert np.all(np.abs(ms - 1.0) <= 2.0 ** -7), ms
+
+
+def pin_norm_rope_quarter_and_half_turn():
+    """A quarter turn maps (a, b) to (-b, a) and a half turn to (-a, -b), exactly."""
+    x, w = _nr_inputs(seed=1)
+    pos = np.zeros(x.shape[0], np.int32)
+    ident = _vals(oracle.norm_rope(x, w, _table(1.0, 0.0), pos, 1e-6))
+    quarter = _vals(oracle.norm_rope(x, w, _table(0.0, 1.0), pos, 1e-6))
+    half = _vals(oracle.norm_rope(x, w, _table(-1.0, 0.0), pos, 1e-6))
+    assert np.array_equal(quarter[..., :HALF], -ident[..., HALF:])
+    assert np.array_equal(quarter[..., HALF:], ident[..., :HALF])
+    assert np.array_equal(half, -ident)
+
+
+def pin_norm_rope_scale_invariance_and_weight_linearity():
+    """RMSNorm ignores a positive scale of x (eps = 0); doubling w doubles the result."""
+    x, w = _nr_inputs(seed=2)
+    tab = _table(0.8, 0.6)
+    pos = np.zeros(x.shape[0], np.int32)
+    base = oracle.norm_rope(x, w, tab, pos, 0.0)
+    x2 = (x.float() * 2).to(torch.bfloat16)  # exact
+    assert np.array_equal(oracle.norm_rope(x2, w, tab, pos, 0.0), base)
+    w2 = (w.float() * 2).to(torch.bfloat16)  # exact
+    assert np.array_equal(_vals(oracle.norm_rope(x, w2, tab, pos, 0.0)), 2 * _vals(base))
+
+
+def pin_norm_rope_heads_independent():
+    x, w = _nr_inputs(seed=3)
+    tab = _table(0.8, 0.6)
+    pos = np.zeros(x.shape[0], np.int32)
+    a = oracle.norm_rope(x, w, tab, pos, 1e-6)
+    x2 = x.clone()
+    x2[:, 1] = (x2[:, 1].float() * -3 + 1).to(torch.bfloat16)
+    b = oracle.norm_rope(x2, w, tab, pos, 1e-6)
+    assert np.array_equal(a[:, [0, 2]], b[:, [0, 2]])
+    assert not np.array_equal(a[:, 1], b[:, 1])
+
+
+def pin_norm_rope_positions_select_rows():
+    """Token t uses table row positions[t], clamped into [0, max_pos)."""
+    x, w = _nr_inputs(T=5, seed=4)
+    rows = [_table(1.0, 0.0), _table(0.0, 1.0), _table(-1.0, 0.0)]
+    tab = np.concatenate(rows)
+    pos = np.array([0, 1, 2, 7, -3], np.int32)
+    got = oracle.norm_rope(x, w, tab, pos, 1e-6)
+    for t, r in enumerate([0, 1, 2, 2, 0]):
+        want = oracle.norm_rope(x[t:t + 1], w, rows[r], np.zeros(1, np.int32), 1e-6)
+        assert np.array_equal(got[t:t + 1], want), t
+
+
+def pin_norm_rope_golden():
+    ex = json.load(open(os.path.join(GOLDEN, "norm_rope_one_hot.json")))
+    for case in ex["cases"]:
+        x = torch.zeros(1, 1, D)
+        x[0, 0, 0] = case["x0"]
+        out = oracle.norm_rope(x.to(torch.bfloat16), torch.ones(D, dtype=torch.bfloat16),
+                               _table(ex["cos"], ex["sin"]), np.zeros(1, np.int32), case["eps"])[0, 0]
+        want = np.zeros(D, np.uint16)
+        for d, b in case["expect"]:
+            want[d] = b
+        assert np.array_equal(out, want), (case, [hex(v) for v in out[[0, 64]]])
+
+
+def pin_narrow_bf16_matches_torch():
+    """On float32 values (where torch's float32 -> bfloat16 conversion rounds
+    once) the oracle's narrowing gives the same bits, subnormals included."""
+    g = torch.Generator().manual_seed(5)
+    v = torch.cat([torch.randn(3000, generator=g) * 10.0 ** torch.randint(-6, 6, (3000,), generator=g),
+                   torch.randn(200, generator=g) * 1e-39,
+                   torch.tensor([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.389e38, 3.4e38, -3.4e38])])
+    want = v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.narrow_bf16(float(a)) for a in v.tolist()], np.uint16)
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:5]
+
+
 PINS = [pin_decode_vs_sdpa, pin_c1_shape_vs_sdpa, pin_block_permutation_invariance, pin_weights_sum_to_one,
         pin_identical_keys_give_mean, pin_zero_query_uniform, pin_single_token, pin_dominant_key,
         pin_equal_queries_in_group, pin_empty_context, pin_prefill_rows_equal_decode, pin_prefill_vs_masked_sdpa,
-        pin_split_merge_identity, pin_merge_all_empty, pin_append_vs_numpy_scatter, pin_golden_examples]
+        pin_split_merge_identity, pin_merge_all_empty, pin_append_vs_numpy_scatter, pin_golden_examples,
+        pin_norm_rope_identity_unit_rms, pin_norm_rope_quarter_and_half_turn,
+        pin_norm_rope_scale_invariance_and_weight_linearity, pin_norm_rope_heads_independent,
+        pin_norm_rope_positions_select_rows, pin_norm_rope_golden, pin_narrow_bf16_matches_torch]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -344,6 +456,16 @@ MUTANTS = {
     "append_offset_reversed": [("* BS + off) * static_cast<size_t>(D);\n      const size_t src",
                                 "* BS + (BS - 1 - off)) * static_cast<size_t>(D);\n      const size_t src")],
     "dot_skips_last_dim": [("for (int d = 0; d < D; ++d) dot +=", "for (int d = 0; d < D - 1; ++d) dot +=")],
+    "rope_sin_sign_flipped": [("y[d] * c - y[half + d] * s", "y[d] * c + y[half + d] * s"),
+                              ("y[half + d] * c + y[d] * s", "y[half + d] * c - y[d] * s")],
+    "rope_cos_sin_swapped": [("const double c = cs[d], s = cs[half + d];", "const double c = cs[half + d], s = cs[d];")],
+    "rope_partner_adjacent": [("y[d] * c - y[half + d] * s", "y[d] * c - y[d ^ 1] * s"),
+                              ("y[half + d] * c + y[d] * s", "y[d ^ 1] * c + y[d] * s")],
+    "rope_position_ignored": [("int p = positions[t];", "int p = 0;")],
+    "rms_mean_over_half": [("std::sqrt(ss / D + eps)", "std::sqrt(ss / half + eps)")],
+    "rms_eps_outside_sqrt": [("1.0 / std::sqrt(ss / D + eps)", "1.0 / std::sqrt(ss / D) + eps")],
+    "norm_weight_dropped": [("* inv_rms * widen_bf16(w[d])", "* inv_rms")],
+    "bf16_rounding_truncates": [("std::nearbyint(std::ldexp(a, shift))", "std::trunc(std::ldexp(a, shift))")],
 }
 
 
