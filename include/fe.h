@@ -74,7 +74,8 @@ typedef enum {
   FE_ERR_UNSUPPORTED = -3,  /* a valid shape this build has no kernel for (D != 128, BS != 16, G > 8) */
   FE_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than the size query returns */
   FE_ERR_HIP = -5,          /* the HIP runtime reported an error at launch */
-  FE_ERR_INTERNAL = -6
+  FE_ERR_INTERNAL = -6,
+  FE_ERR_CAPACITY = -7      /* the KV block allocator has too few free blocks (or a sequence's limit is reached) */
 } fe_status;
 
 /*
@@ -244,6 +245,54 @@ int fe_qk_norm_rope_append(void* q_out, const void* q, const void* k, const void
                            const void* k_norm_w, const float* cos_sin, int max_pos, const int32_t* positions,
                            const int32_t* slot_mapping, void* k_cache, void* v_cache, int T, int Hq, int Hkv, int D,
                            int BS, int num_blocks, float eps, hipStream_t stream);
+
+/*
+ * Paged KV block allocator (host memory, host calls only): hands out the
+ * cache blocks whose slots fe_paged_kv_append fills and whose ids the
+ * attention calls read through block_tables.
+ *   The free blocks form a stack that starts as 0, 1, 2, ... from the top.
+ *   fe_kv_allocator_append pops the blocks a sequence's new tokens need;
+ *   fe_kv_allocator_release pushes all of a sequence's blocks back in reverse
+ *   token order (its first block on top).  Which blocks a call receives
+ *   therefore depends only on the sequence of calls (deterministic cleanup:
+ *   after every sequence is finished or cancelled and released,
+ *   fe_kv_allocator_num_allocated is 0).
+ *   Sequences are ids 0 .. max_seqs - 1, chosen by the caller; each holds at
+ *   most max_blocks_per_seq blocks.  One thread owns an allocator (the
+ *   scheduler): calls on one allocator must not overlap.
+ * Source: ForgeEngine README, "What it implements" (paged block allocator
+ * with deterministic cleanup), "Loading" (one worker owns KV-cache mutation)
+ * and its measurements table (final allocated KV blocks: 0 after finished and
+ * cancelled requests).
+ */
+typedef struct fe_kv_allocator fe_kv_allocator;
+
+/* NULL for non-positive sizes, num_blocks * block_size (or a sequence's
+ * token limit) beyond INT32_MAX, or failed host allocation. */
+fe_kv_allocator* fe_kv_allocator_create(int num_blocks, int block_size, int max_seqs, int max_blocks_per_seq);
+void fe_kv_allocator_destroy(fe_kv_allocator* a);
+
+/* Reserve slots for n new tokens at the end of sequence seq and write them
+ * to slots_out (host int32[n]; slot = block * block_size + offset).  All or
+ * nothing: FE_ERR_CAPACITY when the free blocks or the sequence's block limit
+ * do not suffice (nothing changes); n == 0 is a no-op. */
+int fe_kv_allocator_append(fe_kv_allocator* a, int seq, int n, int32_t* slots_out);
+
+/* Release every block of sequence seq (finished or cancelled); its length
+ * becomes 0.  Releasing an empty sequence is a no-op. */
+int fe_kv_allocator_release(fe_kv_allocator* a, int seq);
+
+/* Tokens held by sequence seq (>= 0), or a negative status. */
+int fe_kv_allocator_seq_len(const fe_kv_allocator* a, int seq);
+int fe_kv_allocator_num_free(const fe_kv_allocator* a);
+int fe_kv_allocator_num_allocated(const fe_kv_allocator* a);
+
+/* Attention inputs for a batch of sequences (host arrays): row i of
+ * block_tables ([n][row_len]) lists seqs[i]'s blocks in token order, padded
+ * with pad_block; context_lens[i] is its length.  FE_ERR_CAPACITY when a
+ * sequence holds more than row_len blocks. */
+int fe_kv_allocator_batch(const fe_kv_allocator* a, const int* seqs, int n, int32_t* block_tables, int row_len,
+                          int32_t pad_block, int32_t* context_lens);
 
 /* Static description of a status code (never NULL). */
 const char* fe_status_string(int status);

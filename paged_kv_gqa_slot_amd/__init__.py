@@ -6,6 +6,15 @@ those calls; the library is loaded on first use and a missing or unbuilt
 library is an error -- there is no CPU fallback.
 """
 from .binding import (  # noqa: F401
+    KVAllocator,
+    fe_kv_allocator_append,
+    fe_kv_allocator_batch,
+    fe_kv_allocator_create,
+    fe_kv_allocator_destroy,
+    fe_kv_allocator_num_allocated,
+    fe_kv_allocator_num_free,
+    fe_kv_allocator_release,
+    fe_kv_allocator_seq_len,
     fe_last_error,
     fe_paged_gqa_decode,
     fe_paged_gqa_decode_num_partitions,

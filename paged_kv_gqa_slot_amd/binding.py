@@ -13,6 +13,7 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +57,22 @@ def load_library():
     lib.fe_paged_gqa_mixed.restype = I
     lib.fe_qk_norm_rope_append.argtypes = [P, P, P, P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, F, P]
     lib.fe_qk_norm_rope_append.restype = I
+    H = ctypes.c_void_p  # fe_kv_allocator*
+    lib.fe_kv_allocator_create.argtypes = [I, I, I, I]
+    lib.fe_kv_allocator_create.restype = H
+    lib.fe_kv_allocator_destroy.argtypes = [H]
+    lib.fe_kv_allocator_destroy.restype = None
+    lib.fe_kv_allocator_append.argtypes = [H, I, I, P]
+    lib.fe_kv_allocator_append.restype = I
+    lib.fe_kv_allocator_release.argtypes = [H, I]
+    lib.fe_kv_allocator_release.restype = I
+    for name in ("fe_kv_allocator_num_free", "fe_kv_allocator_num_allocated"):
+        getattr(lib, name).argtypes = [H]
+        getattr(lib, name).restype = I
+    lib.fe_kv_allocator_seq_len.argtypes = [H, I]
+    lib.fe_kv_allocator_seq_len.restype = I
+    lib.fe_kv_allocator_batch.argtypes = [H, P, I, P, I, ctypes.c_int32, P]
+    lib.fe_kv_allocator_batch.restype = I
     lib.fe_status_string.argtypes = [I]
     lib.fe_status_string.restype = ctypes.c_char_p
     lib.fe_last_error.argtypes = []
@@ -211,3 +228,92 @@ def fe_qk_norm_rope_append(q_out, q, k, v, q_norm_w, k_norm_w, cos_sin, position
         _dev(k_cache, torch.bfloat16, "k_cache", 4), _dev(v_cache, torch.bfloat16, "v_cache", 4), T, Hq, Hkv, D, BS,
         NB, float(eps), _stream(stream))
     _check(rc, "fe_qk_norm_rope_append")
+
+
+# ----------------------------------------------------------------------------
+# paged KV block allocator (host)
+
+def fe_kv_allocator_create(num_blocks: int, block_size: int, max_seqs: int, max_blocks_per_seq: int) -> int:
+    h = load_library().fe_kv_allocator_create(num_blocks, block_size, max_seqs, max_blocks_per_seq)
+    if not h:
+        raise ValueError("fe_kv_allocator_create: invalid sizes")
+    return h
+
+
+def fe_kv_allocator_destroy(h) -> None:
+    load_library().fe_kv_allocator_destroy(h)
+
+
+def fe_kv_allocator_append(h, seq: int, n: int) -> np.ndarray:
+    """Slots (int32 [n]) of n new tokens at the end of sequence seq."""
+    out = np.zeros(max(int(n), 0), np.int32)
+    _check(load_library().fe_kv_allocator_append(h, int(seq), int(n), out.ctypes.data_as(ctypes.c_void_p)),
+           "fe_kv_allocator_append")
+    return out
+
+
+def fe_kv_allocator_release(h, seq: int) -> None:
+    _check(load_library().fe_kv_allocator_release(h, int(seq)), "fe_kv_allocator_release")
+
+
+def fe_kv_allocator_seq_len(h, seq: int) -> int:
+    n = load_library().fe_kv_allocator_seq_len(h, int(seq))
+    _check(min(n, 0), "fe_kv_allocator_seq_len")
+    return n
+
+
+def fe_kv_allocator_num_free(h) -> int:
+    return load_library().fe_kv_allocator_num_free(h)
+
+
+def fe_kv_allocator_num_allocated(h) -> int:
+    return load_library().fe_kv_allocator_num_allocated(h)
+
+
+def fe_kv_allocator_batch(h, seqs, row_len: int, pad_block: int = 0):
+    """(block_tables int32 [n][row_len], context_lens int32 [n]) of the listed sequences."""
+    s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+    bt = np.zeros((s.shape[0], row_len), np.int32)
+    cl = np.zeros(s.shape[0], np.int32)
+    _check(load_library().fe_kv_allocator_batch(h, s.ctypes.data_as(ctypes.c_void_p), s.shape[0],
+                                                bt.ctypes.data_as(ctypes.c_void_p), int(row_len), int(pad_block),
+                                                cl.ctypes.data_as(ctypes.c_void_p)), "fe_kv_allocator_batch")
+    return bt, cl
+
+
+class KVAllocator:
+    """Owning wrapper of an fe_kv_allocator handle (same calls, as methods)."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_seqs: int, max_blocks_per_seq: int):
+        self.handle = None
+        self.handle = fe_kv_allocator_create(num_blocks, block_size, max_seqs, max_blocks_per_seq)
+        self.block_size = block_size
+        self.max_blocks_per_seq = max_blocks_per_seq
+
+    def append(self, seq, n):
+        return fe_kv_allocator_append(self.handle, seq, n)
+
+    def release(self, seq):
+        fe_kv_allocator_release(self.handle, seq)
+
+    def seq_len(self, seq):
+        return fe_kv_allocator_seq_len(self.handle, seq)
+
+    @property
+    def num_free(self):
+        return fe_kv_allocator_num_free(self.handle)
+
+    @property
+    def num_allocated(self):
+        return fe_kv_allocator_num_allocated(self.handle)
+
+    def batch(self, seqs, row_len=None, pad_block=0):
+        return fe_kv_allocator_batch(self.handle, seqs, row_len or self.max_blocks_per_seq, pad_block)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            fe_kv_allocator_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()

@@ -56,6 +56,7 @@ const char* fe_status_string(int status) {
     case FE_ERR_WORKSPACE: return "FE_ERR_WORKSPACE";
     case FE_ERR_HIP: return "FE_ERR_HIP";
     case FE_ERR_INTERNAL: return "FE_ERR_INTERNAL";
+    case FE_ERR_CAPACITY: return "FE_ERR_CAPACITY";
     default: return "FE_ERR_UNKNOWN";
   }
 }
