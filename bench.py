@@ -272,6 +272,67 @@ def bench_norm_rope(args, w, fe, inputs, torch, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_sampler(args, fe, inputs, torch, dev):
+    """fp32 softmax + LSE + greedy argmax over the Qwen3 vocabulary for a batch of rows."""
+    B, V = args.sampler_batch, inputs.QWEN3_VOCAB
+    c = inputs.sampler_case(B, V, seed=args.seed or 1)
+    x, it = c.logits.to(dev), c.inv_temperature.to(dev)
+    probs = torch.empty(B, V, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, dtype=torch.float32, device=dev)
+    am = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(fe.fe_sampler_workspace_size(B, V), 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        fe.fe_sampler_softmax_argmax(probs, lse, am, x, it, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    avg = sum(per) / len(per)
+    nbytes = B * V * 2 + B * V * 4 + B * (4 + 4 + 4)  # logits in, probs out, temperatures, lse, argmax
+    achieved = nbytes / (avg * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "fe_sampler_softmax_argmax (sampler_partial_kernel + sampler_write_kernel)",
+            "per_launch_bytes": nbytes, "avg_ms": round(avg, 5), "median_ms": round(per[len(per) // 2], 5)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = os.cpu_count() or 1
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.sampler(c.logits, c.inv_temperature)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_budget, 10.0) or reps >= 20:
+                break
+        cpu = {"value": round(nbytes / (el / reps) / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"fp64 oracle over all {B} rows of {V} logits, {reps} repetitions, {el / reps * 1e3:.1f} ms each"}
+    cfg = {"workload": f"sampler:qwen3_vocab{V}_b{B}", "batch": B, "vocab": V, "seed": args.seed or 1}
+    rec = {"metric": "fp32 softmax + argmax over the vocabulary, achieved HBM GB/s", "value":
+           round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp32", "data": "synthetic", "config": cfg, "roofline": roof,
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,8 +343,10 @@ def main():
     ap.add_argument("--partitions", type=int, default=0, help="decode split-K factor (0 = automatic)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["attention", "norm_rope"], default="attention",
-                    help="norm_rope: time the fused QK-RMSNorm + rotary + append step on the workload's new tokens")
+    ap.add_argument("--op", choices=["attention", "norm_rope", "sampler"], default="attention",
+                    help="norm_rope: the fused QK-RMSNorm + rotary + append step on the workload's new tokens; "
+                         "sampler: fp32 softmax + argmax over the Qwen3 vocabulary for --sampler-batch rows")
+    ap.add_argument("--sampler-batch", type=int, default=64)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (rocprofv3 counter calibration)")
     args = ap.parse_args()
@@ -300,6 +363,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     fe.load_library()
+    if args.op == "sampler":
+        return bench_sampler(args, fe, inputs, torch, dev)
     log(f"generating workload {args.workload} ...")
     w = inputs.make(args.workload, seed=args.seed)
     spec = w.spec

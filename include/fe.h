@@ -247,6 +247,35 @@ int fe_qk_norm_rope_append(void* q_out, const void* q, const void* k, const void
                            int BS, int num_blocks, float eps, hipStream_t stream);
 
 /*
+ * Bytes of device workspace fe_sampler_softmax_argmax needs for B rows of
+ * V logits (host-only; (size_t)-1 for invalid sizes).
+ */
+size_t fe_sampler_workspace_size(int B, int V);
+
+/*
+ * The sampler's hot step over each row b of bf16 logits [B][V], at inverse
+ * temperature s = inv_temperature[b] (NULL: 1), in fp32:
+ *   probs[b][i] = exp(s x_i - m) / sum_j exp(s x_j - m),  m = max_j s x_j
+ *   lse[b]      = m + log sum_j exp(s x_j - m)            (natural log)
+ *   argmax[b]   = the lowest i with x_i = max_j x_j       (greedy token, exact)
+ *   -inf logits are masked tokens (probability 0); a row of only -inf gives
+ *   probabilities 0, lse = -inf and argmax 0.
+ *   probs          fp32 [B][V], or NULL (argmax / lse only)
+ *   lse            fp32 [B], or NULL
+ *   argmax         int32 [B]
+ *   logits         bf16 [B][V]; V must be a multiple of 8 (FE_ERR_UNSUPPORTED)
+ *   inv_temperature  fp32 [B] (> 0, finite; not checked) or NULL
+ *   workspace      device scratch of fe_sampler_workspace_size(B, V) bytes,
+ *                  clobbered
+ * Source: "Make the Engine Talk" section 1.3 (the sampler: greedy,
+ * temperature and top-p decoding, with its softmax in fp32 over a vocabulary
+ * this wide); ForgeEngine README, "What it implements" (sampling policies).
+ */
+int fe_sampler_softmax_argmax(float* probs, float* lse, int32_t* argmax, const void* logits,
+                              const float* inv_temperature, int B, int V, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * Paged KV block allocator (host memory, host calls only): hands out the
  * cache blocks whose slots fe_paged_kv_append fills and whose ids the
  * attention calls read through block_tables.

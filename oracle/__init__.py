@@ -69,6 +69,8 @@ def _load():
     lib.oracle_prefill_chunk.restype = I
     lib.oracle_qk_norm_rope.argtypes = [P, P, P, P, I, P, I, I, I, Dd, I]
     lib.oracle_qk_norm_rope.restype = I
+    lib.oracle_sampler.argtypes = [P, P, P, P, P, I, I, I]
+    lib.oracle_sampler.restype = I
     lib.oracle_narrow_bf16.argtypes = [Dd]
     lib.oracle_narrow_bf16.restype = ctypes.c_uint16
     _lib = lib
@@ -216,3 +218,19 @@ def qk_norm_rope_append(q, k, v, q_norm_w, k_norm_w, cos_sin, positions, slot_ma
 def narrow_bf16(v: float) -> int:
     """Nearest-even bf16 bits of a double (the oracle's own rounding)."""
     return int(_load().oracle_narrow_bf16(float(v)))
+
+
+def sampler(logits, inv_temp=None, with_probs=True, nthreads=None):
+    """fp64 softmax / log-sum-exp / greedy argmax of bf16 logits [B][V] at
+    per-row inverse temperatures.  Returns (probs [B][V] or None, lse [B], argmax [B] int32)."""
+    x = _bits(logits)
+    B, V = x.shape
+    it = None if inv_temp is None else _f32(inv_temp)
+    probs = np.zeros((B, V), np.float64) if with_probs else None
+    lse = np.zeros(B, np.float64)
+    am = np.zeros(B, np.int32)
+    rc = _load().oracle_sampler(_ptr(probs) if probs is not None else None, _ptr(lse), _ptr(am), _ptr(x),
+                                _ptr(it) if it is not None else None, B, V, _threads(nthreads))
+    if rc:
+        raise ValueError(f"oracle_sampler rejected the sizes (status {rc})")
+    return probs, lse, am

@@ -36,6 +36,15 @@
 // cosine and sine the caller's table holds at [position][d] and
 // [position][D/2 + d]; the result is rounded once to bf16 (nearest even).
 //
+// The sampler's hot step ("Make the Engine Talk" section 1.3: the sampler,
+// greedy, temperature and top-p decoding, with its softmax in fp32 over the
+// whole vocabulary; ForgeEngine README, "What it implements": sampling
+// policies): per row of bf16 logits x and inverse temperature s,
+// p_i = exp(s x_i - m) / sum_j exp(s x_j - m) with m = max_j s x_j, the
+// natural-log lse = m + log sum_j exp(s x_j - m), and the greedy token
+// argmax_i x_i (the lowest index among equal maxima; -inf entries are
+// masked tokens; a row of only -inf gives p = 0, lse = -inf, argmax 0).
+//
 // Arithmetic: every bf16 value widens exactly to double; scale is the caller's
 // value; dot products sum in increasing d, softmax sums in increasing t; the
 // softmax is the two-pass max-shifted definition.  No blocking or reordering.
@@ -56,6 +65,7 @@
 // identity; append against a NumPy scatter.
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <limits>
 #include <thread>
@@ -330,6 +340,42 @@ int oracle_qk_norm_rope(uint16_t* out, const uint16_t* x, const uint16_t* w, con
       o[d] = narrow_bf16(y[d] * c - y[half + d] * s);
       o[half + d] = narrow_bf16(y[half + d] * c + y[d] * s);
     }
+  });
+  return 0;
+}
+
+// Softmax, log-sum-exp and greedy argmax of each row of bf16 logits
+// [B][V] at inverse temperature inv_temp[b] (> 0; NULL = 1).  probs may be
+// NULL.  Returns 0, or -1 for bad sizes.
+int oracle_sampler(double* probs, double* lse, int32_t* argmax, const uint16_t* logits, const float* inv_temp, int B,
+                   int V, int nthreads) {
+  if (B < 0 || V <= 0) return -1;
+  parallel_for(B, nthreads, [&](int b) {
+    const uint16_t* x = logits + static_cast<size_t>(b) * V;
+    const double s = inv_temp ? static_cast<double>(inv_temp[b]) : 1.0;
+    int best = 0;
+    double bestv = widen_bf16(x[0]);
+    for (int i = 1; i < V; ++i) {
+      const double v = widen_bf16(x[i]);
+      if (v > bestv) {
+        bestv = v;
+        best = i;
+      }
+    }
+    argmax[b] = best;
+    double m = -std::numeric_limits<double>::infinity();
+    for (int i = 0; i < V; ++i) m = std::max(m, s * widen_bf16(x[i]));
+    if (m == -std::numeric_limits<double>::infinity()) {  // every token masked
+      lse[b] = m;
+      if (probs)
+        for (int i = 0; i < V; ++i) probs[static_cast<size_t>(b) * V + i] = 0.0;
+      return;
+    }
+    double Z = 0.0;
+    for (int i = 0; i < V; ++i) Z += std::exp(s * widen_bf16(x[i]) - m);
+    lse[b] = m + std::log(Z);
+    if (probs)
+      for (int i = 0; i < V; ++i) probs[static_cast<size_t>(b) * V + i] = std::exp(s * widen_bf16(x[i]) - m) / Z;
   });
   return 0;
 }

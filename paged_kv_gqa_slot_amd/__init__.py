@@ -24,6 +24,8 @@ from .binding import (  # noqa: F401
     fe_paged_gqa_prefill_chunk,
     fe_paged_kv_append,
     fe_qk_norm_rope_append,
+    fe_sampler_softmax_argmax,
+    fe_sampler_workspace_size,
     fe_status_string,
     library_path,
     load_library,

@@ -73,6 +73,10 @@ def load_library():
     lib.fe_kv_allocator_seq_len.restype = I
     lib.fe_kv_allocator_batch.argtypes = [H, P, I, P, I, ctypes.c_int32, P]
     lib.fe_kv_allocator_batch.restype = I
+    lib.fe_sampler_workspace_size.argtypes = [I, I]
+    lib.fe_sampler_workspace_size.restype = Z
+    lib.fe_sampler_softmax_argmax.argtypes = [P, P, P, P, P, I, I, P, Z, P]
+    lib.fe_sampler_softmax_argmax.restype = I
     lib.fe_status_string.argtypes = [I]
     lib.fe_status_string.restype = ctypes.c_char_p
     lib.fe_last_error.argtypes = []
@@ -228,6 +232,27 @@ def fe_qk_norm_rope_append(q_out, q, k, v, q_norm_w, k_norm_w, cos_sin, position
         _dev(k_cache, torch.bfloat16, "k_cache", 4), _dev(v_cache, torch.bfloat16, "v_cache", 4), T, Hq, Hkv, D, BS,
         NB, float(eps), _stream(stream))
     _check(rc, "fe_qk_norm_rope_append")
+
+
+def fe_sampler_workspace_size(B: int, V: int) -> int:
+    n = load_library().fe_sampler_workspace_size(int(B), int(V))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("fe_sampler_workspace_size: invalid sizes")
+    return int(n)
+
+
+def fe_sampler_softmax_argmax(probs, lse, argmax, logits, inv_temperature=None, workspace=None, stream=None) -> None:
+    """fp32 softmax (probs may be None), LSE (may be None) and greedy argmax of bf16 logits [B][V]."""
+    B, V = logits.shape
+    ws_bytes = fe_sampler_workspace_size(B, V)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=logits.device)
+    rc = load_library().fe_sampler_softmax_argmax(
+        _dev(probs, torch.float32, "probs", 2), _dev(lse, torch.float32, "lse", 1),
+        _dev(argmax, torch.int32, "argmax", 1), _dev(logits, torch.bfloat16, "logits", 2),
+        _dev(inv_temperature, torch.float32, "inv_temperature", 1), B, V, _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream))
+    _check(rc, "fe_sampler_softmax_argmax")
 
 
 # ----------------------------------------------------------------------------

@@ -226,4 +226,31 @@ int fe_qk_norm_rope_append(void* q_out, const void* q, const void* k, const void
   }
 }
 
+size_t fe_sampler_workspace_size(int B, int V) {
+  if (B < 0 || V <= 0 || V % 8 != 0) return static_cast<size_t>(-1);
+  return fe::plan_sampler(B, V).workspace_bytes;
+}
+
+int fe_sampler_softmax_argmax(float* probs, float* lse, int32_t* argmax, const void* logits,
+                              const float* inv_temperature, int B, int V, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  static const char* fn = "fe_sampler_softmax_argmax";
+  try {
+    if (B < 0 || V <= 0) return fail(FE_ERR_INVALID_ARG, fn, "B must be >= 0 and V positive");
+    if (V % 8 != 0) return fail(FE_ERR_UNSUPPORTED, fn, "V must be a multiple of 8");
+    if (B == 0) return FE_OK;
+    if (!argmax || !logits) return fail(FE_ERR_NULL, fn, "argmax and logits must not be NULL");
+    if (!aligned16(logits) || !aligned16(probs))
+      return fail(FE_ERR_INVALID_ARG, fn, "logits and probs must be 16-byte aligned");
+    const fe::SamplerPlan plan = fe::plan_sampler(B, V);
+    if (!workspace || workspace_bytes < plan.workspace_bytes)
+      return fail(FE_ERR_WORKSPACE, fn, "workspace missing or smaller than fe_sampler_workspace_size()");
+    const fe::SamplerArgs a{probs, lse, argmax, logits, inv_temperature, B, V, plan, workspace};
+    const hipError_t e = fe::launch_sampler(a, stream);
+    return e == hipSuccess ? FE_OK : hip_fail(e, fn);
+  } catch (...) {
+    return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
+  }
+}
+
 }  // extern "C"

@@ -100,11 +100,36 @@ struct NormRopeArgs {
   float eps;
 };
 
+// Sampler plan: each row of V logits is cut into `chunks` ranges of
+// `chunk_units` 8-logit units; the workspace holds one 16-byte partial per
+// (row, range).
+struct SamplerPlan {
+  int chunks;
+  int chunk_units;
+  size_t workspace_bytes;
+};
+constexpr int kSamplerTargetWgs = 1024;  // about 4 workgroups per CU
+constexpr int kSamplerMinUnits = 512;    // ranges of at least 4096 logits
+constexpr int kSamplerMaxUnits = 2048;   // ... and at most 16384 (8 units per thread)
+SamplerPlan plan_sampler(int B, int V);
+
+struct SamplerArgs {
+  float* probs;
+  float* lse;
+  int32_t* argmax;
+  const void* logits;
+  const float* inv_temperature;
+  int B, V;
+  SamplerPlan plan;
+  void* workspace;
+};
+
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_cache,
                             void* v_cache, int T, int num_blocks, int Hkv, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_mixed(const MixedArgs& a, hipStream_t stream);
 hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream);
+hipError_t launch_sampler(const SamplerArgs& a, hipStream_t stream);
 
 }  // namespace fe

@@ -44,6 +44,7 @@ def fp32_scale(head_dim: int = D) -> float:
 # one size does not shift the others.
 _LEN, _PERM, _Q, _K, _V, _SPIKE = 1, 2, 3, 4, 5, 6
 _NR_Q, _NR_K, _NR_V, _NR_W = 7, 8, 9, 10  # inputs of the norm/rotary step
+_SM_X, _SM_PEAK = 11, 12                   # inputs of the sampler step
 
 
 def _gen(seed: int, stream: int, layer: int = 0) -> torch.Generator:
@@ -333,3 +334,29 @@ def norm_rope_case(w: Workload, seed: int, max_pos: Optional[int] = None) -> Nor
     return NormRopeCase(q=q, k=k, v=v, q_norm_w=ww[0].to(torch.bfloat16), k_norm_w=ww[1].to(torch.bfloat16),
                         cos_sin=rope_table(max_pos), positions=pos, slot_mapping=w.slot_mapping.clone(),
                         k_cache=w.layers[0].k_cache, v_cache=w.layers[0].v_cache)
+
+
+# ----------------------------------------------------------------------------
+# Inputs of the sampler step (softmax / argmax over the vocabulary).
+
+QWEN3_VOCAB = 151936
+TEMPERATURES = (0.6, 0.7, 1.0, 1.3)  # cycled over the rows
+
+
+@dataclass
+class SamplerCase:
+    logits: torch.Tensor           # bf16 [B][V]
+    inv_temperature: torch.Tensor  # fp32 [B]
+
+
+def sampler_case(B: int, V: int = QWEN3_VOCAB, seed: int = 1, peaks: int = 5) -> SamplerCase:
+    """Language-model-like logits: 2.5 * randn, plus `peaks` tokens per row
+    raised by 8..16 (the likely next tokens); rows cycle through TEMPERATURES."""
+    g = _gen(seed, _SM_X)
+    x = 2.5 * torch.randn((B, V), generator=g, dtype=torch.float32)
+    if peaks and V:
+        gp = _gen(seed, _SM_PEAK)
+        idx = torch.randint(0, V, (B, peaks), generator=gp)
+        x.scatter_add_(1, idx, 8.0 + 8.0 * torch.rand((B, peaks), generator=gp))
+    it = torch.tensor([1.0 / TEMPERATURES[b % len(TEMPERATURES)] for b in range(B)], dtype=torch.float32)
+    return SamplerCase(logits=x.to(torch.bfloat16), inv_temperature=it)

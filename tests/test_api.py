@@ -228,3 +228,24 @@ def test_misaligned_pointers_rejected(lib):
     assert dec(lib, q=P + 8) == INVALID
     assert pre(lib, out=P + 2) == INVALID
     assert mix(lib, k=P + 4) == INVALID
+
+
+def smp(lib, **kw):
+    a = dict(probs=P, lse=P, am=P, x=P, it=None, B=4, V=1024, ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.fe_sampler_softmax_argmax(a["probs"], a["lse"], a["am"], a["x"], a["it"], a["B"], a["V"], a["ws"],
+                                         a["wsb"], a["stream"])
+
+
+def test_sampler_argument_errors(lib):
+    assert smp(lib, am=None) == NULL
+    assert smp(lib, x=None) == NULL
+    assert smp(lib, B=-1) == INVALID
+    assert smp(lib, V=0) == INVALID
+    assert smp(lib, V=1001) == UNSUPPORTED
+    assert smp(lib, ws=None) == WORKSPACE
+    need = lib.fe_sampler_workspace_size(4, 151936)
+    assert need > 0 and smp(lib, V=151936, wsb=need - 1) == WORKSPACE
+    assert smp(lib, x=P + 2) == INVALID
+    assert smp(lib, B=0, x=None, am=None) == OK
+    assert lib.fe_sampler_workspace_size(4, 1001) == ctypes.c_size_t(-1).value

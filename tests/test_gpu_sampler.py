@@ -1,0 +1,82 @@
+"""GPU parity of the sampler step (fe_sampler_softmax_argmax) against the
+fp64 oracle.
+
+Gate, from the arithmetic: the kernel evaluates 2^(s x log2 e - m) in fp32;
+the exponent argument carries an absolute error of about |s x log2 e| 2^-23
+(at most ~70 here, so ~1e-5 relative on a probability after exp2), the sum
+of ~150k terms a relative error of a few 1e-6, and exp2 and the final
+product one ulp each: about 2e-5 relative in all.  Probabilities must be
+within 1e-4 relative (plus 1e-37 absolute, for values fp32 flushes or
+underflows), the LSE within 1e-4, and the argmax -- an exact comparison of
+the bf16 logits on both sides -- must be identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_gqa_slot_amd as fe
+from paged_kv_gqa_slot_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+REL, ABS, LSE_ABS = 1e-4, 1e-37, 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def run(c: inputs.SamplerCase, dev, label, with_probs=True, temps=True):
+    B, V = c.logits.shape
+    x = c.logits.to(dev)
+    it = c.inv_temperature.to(dev) if temps else None
+    probs = torch.full((B, V), float("nan"), dtype=torch.float32, device=dev) if with_probs else None
+    lse = torch.full((B,), float("nan"), dtype=torch.float32, device=dev)
+    am = torch.full((B,), -1, dtype=torch.int32, device=dev)
+    fe.fe_sampler_softmax_argmax(probs, lse, am, x, it)
+    torch.cuda.synchronize()
+    rp, rl, ra = oracle.sampler(c.logits, c.inv_temperature if temps else None, with_probs=with_probs)
+    assert np.array_equal(am.cpu().numpy(), ra), (label, "argmax")
+    gl = lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl)), (label, "lse -inf pattern")
+    fin = ~np.isneginf(rl)
+    lerr = float(np.abs(gl[fin] - rl[fin]).max()) if fin.any() else 0.0
+    assert lerr <= LSE_ABS, (label, "lse", lerr)
+    if with_probs:
+        gp = probs.cpu().numpy().astype(np.float64)
+        err = np.abs(gp - rp)
+        ok = err <= REL * rp + ABS
+        worst = float((err / (REL * rp + ABS)).max())
+        print(f"[{label}] worst err/bound {worst:.3f}, lse err {lerr:.2e}", flush=True)
+        assert ok.all(), (label, "probs", worst)
+
+
+@pytest.mark.parametrize("B,V", [(1, 8), (3, 16), (5, 1000), (64, 4104), (2, 40000)])
+def test_sampler_small(dev, B, V):
+    run(inputs.sampler_case(B, V, seed=B + V, peaks=min(5, V)), dev, f"B={B} V={V}")
+
+
+def test_sampler_masked_rows_and_ties(dev):
+    c = inputs.sampler_case(4, 4096, seed=3)
+    x = c.logits.float()
+    x[0, ::3] = float("-inf")                  # a third of the tokens masked
+    x[1, :] = float("-inf")                    # every token masked
+    x[2, [5, 900, 4095]] = 60.0                # three-way tie at the max: the lowest index wins
+    x[3, :] = 1.25                             # all equal: index 0, uniform probabilities
+    c.logits = x.to(torch.bfloat16)
+    run(c, dev, "masked / ties")
+
+
+def test_sampler_no_temperature_and_no_probs(dev):
+    c = inputs.sampler_case(6, 12000, seed=4)
+    run(c, dev, "no temperature", temps=False)
+    run(c, dev, "argmax and lse only", with_probs=False)
+
+
+def test_sampler_qwen3_vocab_batch64(dev):
+    """The sampler step of the 64-sequence decode batch over the full Qwen3 vocabulary."""
+    run(inputs.sampler_case(64, inputs.QWEN3_VOCAB, seed=5), dev, "Qwen3 vocab B=64")

@@ -424,13 +424,65 @@ def pin_narrow_bf16_matches_torch():
     assert np.array_equal(got, want), np.nonzero(got != want)[0][:5]
 
 
+# ----------------------------------------------------------------------------
+# the sampler's softmax / log-sum-exp / greedy argmax (f4)
+
+def _logits(B=4, V=3000, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    return (3.0 * torch.randn(B, V, generator=g)).to(torch.bfloat16)
+
+
+def pin_sampler_vs_torch_softmax():
+    """torch's float64 softmax and logsumexp, at several temperatures."""
+    x = _logits()
+    it = np.array([1.0, 0.5, 1.7, 3.0], np.float32)
+    p, lse, _ = oracle.sampler(x, it)
+    z = x.double() * torch.from_numpy(it).double()[:, None]
+    assert np.allclose(p, torch.softmax(z, -1).numpy(), rtol=1e-12, atol=1e-300)
+    assert np.allclose(lse, torch.logsumexp(z, -1).numpy(), rtol=0, atol=1e-12)
+
+
+def pin_sampler_argmax_first_of_ties():
+    x = _logits(B=3, V=500, seed=1).float()
+    x[0, 7] = x[0, 300] = x[0, 499] = 40.0       # tie at the max: lowest index wins
+    x[1, :] = 2.0                                # all equal
+    x[2, 499] = 50.0                             # the last entry
+    x = x.to(torch.bfloat16)
+    _, _, am = oracle.sampler(x, with_probs=False)
+    assert am.tolist() == [7, 0, 499]
+    assert am[0] == int(np.argmax(x.float().numpy()[0]))  # numpy returns the first maximum too
+
+
+def pin_sampler_masked_and_uniform():
+    V = 1000
+    x = torch.full((3, V), 1.5)
+    x[1, ::2] = float("-inf")                    # half the tokens masked
+    x[2, :] = float("-inf")                      # every token masked
+    p, lse, am = oracle.sampler(x.to(torch.bfloat16), np.array([2.0, 1.0, 1.0], np.float32))
+    assert np.allclose(p[0], 1.0 / V, rtol=1e-14) and abs(lse[0] - (3.0 + math.log(V))) < 1e-12
+    assert np.all(p[1, ::2] == 0.0) and np.allclose(p[1, 1::2], 2.0 / V, rtol=1e-14)
+    assert abs(lse[1] - (1.5 + math.log(V / 2))) < 1e-12
+    assert np.all(p[2] == 0.0) and lse[2] == -math.inf and am[2] == 0
+
+
+def pin_sampler_temperature_scale_identity():
+    """Doubling the logits (exact in bf16) at half the inverse temperature changes nothing."""
+    x = _logits(B=2, V=777, seed=2)
+    x2 = (x.float() * 2).to(torch.bfloat16)
+    a = oracle.sampler(x, np.array([1.0, 0.8], np.float32))
+    b = oracle.sampler(x2, np.array([0.5, 0.4], np.float32))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+
+
 PINS = [pin_decode_vs_sdpa, pin_c1_shape_vs_sdpa, pin_block_permutation_invariance, pin_weights_sum_to_one,
         pin_identical_keys_give_mean, pin_zero_query_uniform, pin_single_token, pin_dominant_key,
         pin_equal_queries_in_group, pin_empty_context, pin_prefill_rows_equal_decode, pin_prefill_vs_masked_sdpa,
         pin_split_merge_identity, pin_merge_all_empty, pin_append_vs_numpy_scatter, pin_golden_examples,
         pin_norm_rope_identity_unit_rms, pin_norm_rope_quarter_and_half_turn,
         pin_norm_rope_scale_invariance_and_weight_linearity, pin_norm_rope_heads_independent,
-        pin_norm_rope_positions_select_rows, pin_norm_rope_golden, pin_narrow_bf16_matches_torch]
+        pin_norm_rope_positions_select_rows, pin_norm_rope_golden, pin_narrow_bf16_matches_torch,
+        pin_sampler_vs_torch_softmax, pin_sampler_argmax_first_of_ties, pin_sampler_masked_and_uniform,
+        pin_sampler_temperature_scale_identity]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -466,6 +518,10 @@ MUTANTS = {
     "rms_eps_outside_sqrt": [("1.0 / std::sqrt(ss / D + eps)", "1.0 / std::sqrt(ss / D) + eps")],
     "norm_weight_dropped": [("* inv_rms * widen_bf16(w[d])", "* inv_rms")],
     "bf16_rounding_truncates": [("std::nearbyint(std::ldexp(a, shift))", "std::trunc(std::ldexp(a, shift))")],
+    "argmax_takes_last_tie": [("      if (v > bestv) {", "      if (v >= bestv) {")],
+    "temperature_ignored": [("const double s = inv_temp ? static_cast<double>(inv_temp[b]) : 1.0;", "const double s = 1.0;")],
+    "sampler_lse_missing_max": [("lse[b] = m + std::log(Z);", "lse[b] = std::log(Z);")],
+    "sampler_probs_unnormalised": [("std::exp(s * widen_bf16(x[i]) - m) / Z;", "std::exp(s * widen_bf16(x[i]) - m);")],
 }
 
 
