@@ -110,6 +110,8 @@ def time_separate_calls(fe, torch, w, x, nd, qsl, bt, lens, mcl, steps, stream) 
 
 
 KERNEL_SOURCES = {
+    "norm_rope": ["qk_norm_rope.hip", "fe_device.h"],
+    "sampler": ["sampler.hip", "fe_device.h"],
     "decode": ["decode.hip", "decode_body.h", "fe_device.h"],
     "prefill": ["prefill.hip", "prefill_body.h", "fe_device.h"],
     "mixed": ["mixed.hip", "decode_body.h", "prefill_body.h", "fe_device.h"],
@@ -198,6 +200,21 @@ def cpu_baseline(w, budget_s: float):
                       f"({el:.1f} s); flops counted for those rows"}
 
 
+def calibrate_copies(args, torch, dev):
+    """After timing: 3 plain device copies of --calibrate-copy-mib MiB, whose
+    rocprofv3 FETCH_SIZE / WRITE_SIZE scale the counters of the kernels."""
+    if args.calibrate_copy_mib <= 0:
+        return
+    n = args.calibrate_copy_mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    log(f"ran 3 device copies of {args.calibrate_copy_mib} MiB for counter calibration")
+
+
 def norm_rope_bytes(T: int, Hq: int, Hkv: int) -> int:
     """Algorithmic HBM bytes of one fused norm/rotary/append call: read q, k,
     v and each token's table row (fp32, 128 entries) plus its position and
@@ -243,9 +260,10 @@ def bench_norm_rope(args, w, fe, inputs, torch, dev):
     nbytes = norm_rope_bytes(T, w.Hq, w.Hkv)
     achieved = nbytes / (avg * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"norm_rope:{w.spec.name}", "norm_rope", 0),
             "kernel": "fe_qk_norm_rope_append (qk_norm_rope_kernel)", "per_launch_bytes": nbytes,
             "avg_ms": round(avg, 5), "median_ms": round(per[len(per) // 2], 5)}
+    calibrate_copies(args, torch, dev)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -307,9 +325,10 @@ def bench_sampler(args, fe, inputs, torch, dev):
     nbytes = B * V * 2 + B * V * 4 + B * (4 + 4 + 4)  # logits in, probs out, temperatures, lse, argmax
     achieved = nbytes / (avg * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"sampler:qwen3_vocab{V}_b{B}", "sampler", 0),
             "kernel": "fe_sampler_softmax_argmax (sampler_partial_kernel + sampler_write_kernel)",
             "per_launch_bytes": nbytes, "avg_ms": round(avg, 5), "median_ms": round(per[len(per) // 2], 5)}
+    calibrate_copies(args, torch, dev)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -494,15 +513,7 @@ def main():
         unit = "TFLOP/s"
         extra = {}
 
-    if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"ran 3 device copies of {args.calibrate_copy_mib} MiB for counter calibration")
+    calibrate_copies(args, torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:

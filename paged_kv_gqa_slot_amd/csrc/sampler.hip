@@ -74,7 +74,9 @@ __global__ __launch_bounds__(kThreads) void sampler_partial_kernel(SamplerParams
 #pragma unroll
   for (int k = 0; k < kUnitsPerThread; ++k) {
     const int u = u0 + threadIdx.x + k * kThreads;
-    w[k] = u < u1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(&row[u])) : u32x4_t{0, 0, 0, 0};
+    // plain (cached) loads: pass 2 reads the same logits again, on the same
+    // XCD (same grid mapping), and finds them in its L2
+    w[k] = u < u1 ? *reinterpret_cast<const u32x4_t*>(&row[u]) : u32x4_t{0, 0, 0, 0};
   }
 #pragma unroll
   for (int k = 0; k < kUnitsPerThread; ++k) {
