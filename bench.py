@@ -8,8 +8,11 @@ serving concurrency: 64 sequences, 32 query / 8 KV heads, head_dim 128, 16-token
 blocks, context lengths 1024..8192 (seeded, synthetic).
 
 Prints one JSON line.  `value` is algorithmic HBM bytes per step / step time
-in GB/s; `roofline` is for the decode call, timed with HIP events on the
-stream its kernels run on; `cpu_baseline` is the fp64 oracle on the host.
+in GB/s, with the step launched the faster of two ways a serving loop would
+use -- every call from the host, or the whole step replayed from a captured
+HIP graph (both times are in the line; --eager skips the graph); `roofline` is for the decode call, timed with HIP
+events on the stream its kernels run on; `cpu_baseline` is the fp64 oracle on
+the host.
 
 Other workloads (--workload): the chunked-prefill one reports TFLOP/s against
 the bf16 MFMA peak; the mixed one (decode rows and prefill chunks in one
@@ -362,6 +365,8 @@ def main():
     ap.add_argument("--partitions", type=int, default=0, help="decode split-K factor (0 = automatic)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call from the host each step instead of replaying a captured HIP graph")
     ap.add_argument("--op", choices=["attention", "norm_rope", "sampler"], default="attention",
                     help="norm_rope: the fused QK-RMSNorm + rotary + append step on the workload's new tokens; "
                          "sampler: fp32 softmax + argmax over the Qwen3 vocabulary for --sampler-batch rows")
@@ -440,16 +445,38 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+
+    def time_steps(fn):
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
     log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    eager_ms = time_steps(step)
+    ms_per_step = eager_ms
+    launch = "eager"
+    if not args.eager:
+        # the whole step (every append and attention call of every layer) as
+        # one captured HIP graph, replayed per step; nothing in these calls
+        # allocates, synchronises or clears memory
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        graph_ms = time_steps(graph.replay)
+        # a serving loop picks the faster way to launch a step of this shape:
+        # replay wins when launches dominate, a tiny step runs faster eagerly
+        if graph_ms < eager_ms:
+            ms_per_step, launch = graph_ms, "hip_graph"
+    else:
+        graph_ms = None
 
     # per-kernel timing of the attention call (the dominant kernel), same stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -522,7 +549,9 @@ def main():
 
     cfg = {"workload": spec.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": 128,
            "block_size": 16, "layers": nl, "kv_tokens": w.kv_tokens, "max_context_len": mcl,
-           "append_tokens_per_step": int(slots.numel()) * nl, "num_partitions": P, "seed": w.seed}
+           "append_tokens_per_step": int(slots.numel()) * nl, "num_partitions": P, "seed": w.seed,
+           "launch": launch, "eager_ms_per_step": round(eager_ms, 5),
+           "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None}
     rec = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": not is_mixed,
            "scaling": "weak",

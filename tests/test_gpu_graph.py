@@ -1,0 +1,105 @@
+"""The calls captured in a HIP graph (the way a serving loop replays its
+step): every replay, with other GPU work run eagerly in between, must give
+exactly the results of the same calls launched eagerly (the kernels reduce in
+a fixed order, so the outputs are bit-identical).  Covers KV append + split-K
+decode (pass 1 + merge), the mixed launch (in-kernel merge through the
+workspace counters) and the fused norm/rotary/append step."""
+import pytest
+import torch
+
+import paged_kv_gqa_slot_amd as fe
+from paged_kv_gqa_slot_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def replay_matches(step, outputs, dev, replays=3, updated=()):
+    """Run step eagerly, capture it, then replay it several times; after each
+    replay the outputs must equal the eager ones bit for bit.  `outputs` are
+    fully written by the step (poisoned before each replay); `updated` are
+    tensors it changes in part (reset to their state before the step)."""
+    before = [u.clone() for u in updated]
+    step()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in list(outputs) + list(updated)]
+    for u, b in zip(updated, before):
+        u.copy_(b)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    noise = torch.randn(1 << 20, device=dev)
+    for r in range(replays):
+        for o in outputs:
+            o.fill_(float("nan")) if o.is_floating_point() else o.fill_(-1)
+        for u, b in zip(updated, before):
+            u.copy_(b)
+        torch.cuda.synchronize()
+        g.replay()
+        noise.mul_(1.0001).add_(0.5)  # eager work between replays
+        torch.cuda.synchronize()
+        for o, w in zip(list(outputs) + list(updated), want):
+            assert torch.equal(o, w) or (o.is_floating_point() and torch.equal(o.isnan(), w.isnan())
+                                         and torch.equal(torch.nan_to_num(o), torch.nan_to_num(w))), r
+
+
+def test_graph_append_and_split_decode(dev):
+    w = inputs.custom("decode", 6, 32, 8, [700, 1500, 64, 999, 3000, 17], 801, append=1)
+    lay = w.layers[0]
+    kc, vc = lay.k_cache.to(dev), lay.v_cache.to(dev)
+    kn, vn, sm = lay.k_new.to(dev), lay.v_new.to(dev), w.slot_mapping.to(dev)
+    q, bt, cl = lay.q.to(dev), w.block_tables.to(dev), w.context_lens.to(dev)
+    out = torch.empty(6, 32, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(6, 32, dtype=torch.float32, device=dev)
+    ws = torch.zeros(fe.fe_paged_gqa_decode_workspace_size(6, 32, 8, 128, w.max_context_len, 8), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fe.fe_paged_kv_append(kn, vn, sm, kc, vc)
+        fe.fe_paged_gqa_decode(out, lse, q, kc, vc, bt, cl, w.max_context_len, w.scale, num_partitions=8,
+                               workspace=ws)
+
+    replay_matches(step, [out, lse], dev, updated=[kc, vc])
+
+
+def test_graph_mixed(dev):
+    w = inputs.custom("mixed", 5, 32, 8, [3000, 1500, 64, 17, 700], 802, append=40, chunk=40, num_decode=3)
+    lay = w.layers[0]
+    kc, vc = lay.k_cache.to(dev), lay.v_cache.to(dev)
+    kn, vn, sm = lay.k_new.to(dev), lay.v_new.to(dev), w.slot_mapping.to(dev)
+    q, qsl = lay.q.to(dev), w.query_start_loc.to(dev)
+    bt, cl = w.block_tables.to(dev), w.context_lens.to(dev)
+    total_q = q.shape[0]
+    out = torch.empty(total_q, 32, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(total_q, 32, dtype=torch.float32, device=dev)
+    ws = torch.zeros(fe.fe_paged_gqa_mixed_workspace_size(3, 32, 8, 128, w.max_context_len, 6), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fe.fe_paged_kv_append(kn, vn, sm, kc, vc)
+        fe.fe_paged_gqa_mixed(out, lse, q, qsl, kc, vc, bt, cl, 3, 40, w.max_context_len, w.scale, num_partitions=6,
+                              workspace=ws)
+
+    replay_matches(step, [out, lse], dev, updated=[kc, vc])
+    assert int(ws[: 3 * 8 * 4].view(torch.int32).abs().sum()) == 0
+
+
+def test_graph_norm_rope(dev):
+    w = inputs.custom("prefill", 3, 32, 8, [100, 40, 300], 803, append=33, chunk=33)
+    c = inputs.norm_rope_case(w, 803)
+    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+    qw, kw, cs = c.q_norm_w.to(dev), c.k_norm_w.to(dev), c.cos_sin.to(dev)
+    pos, sm = c.positions.to(dev), c.slot_mapping.to(dev)
+    kc, vc = c.k_cache.to(dev), c.v_cache.to(dev)
+    q_out = torch.empty_like(q)
+
+    def step():
+        fe.fe_qk_norm_rope_append(q_out, q, k, v, qw, kw, cs, pos, sm, kc, vc, c.eps)
+
+    replay_matches(step, [q_out], dev, updated=[kc, vc])
