@@ -24,9 +24,11 @@
 // The MFMA sums over keys in any order as long as A and B agree, so the
 // k-slot -> key order of each PV step is chosen to match the keys the S^T
 // accumulator layout leaves in each lane (no data movement for P).
-// LDS rows are padded (K: 272 bytes, V: 288 bytes) so that the K row reads of
-// 16 consecutive keys and the 4-key transposed V reads are free of bank
-// conflicts, and every LDS offset is a per-lane base plus a constant.
+// LDS rows are padded (K: 272 bytes, V: 320 bytes) so that the K row reads of
+// 16 consecutive keys (rows 4 banks apart) and the transposed V reads (32
+// lanes reading 64 bytes of 4 rows, rows 16 banks apart) are free of bank
+// conflicts on the 64 banks, and every LDS offset is a per-lane base plus a
+// constant.
 //
 // Schedule.  A tile's work is split into two phases separated by workgroup
 // barriers: an MFMA phase (S^T of tile i, then O^T += V^T P^T of tile i - 1)
@@ -50,9 +52,9 @@ namespace pre {
 constexpr int kKeysPerTile = 64;
 constexpr int kRowBytes = kHeadDim * 2;                 // 256 bytes of one K/V row
 constexpr int kKStride = kRowBytes + 16;                // padded LDS row strides
-constexpr int kVStride = kRowBytes + 32;
+constexpr int kVStride = kRowBytes + 64;
 constexpr int kKTileBytes = kKeysPerTile * kKStride;    // 17408
-constexpr int kVTileBytes = kKeysPerTile * kVStride;    // 18432
+constexpr int kVTileBytes = kKeysPerTile * kVStride;    // 20480
 constexpr int kBufBytes = kKTileBytes + kVTileBytes;    // one K + V tile
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kEmptyMax = -1.0e30f;
