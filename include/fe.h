@@ -31,9 +31,12 @@
  *
  * Conventions:
  *   - Every pointer argument is DEVICE memory owned by the caller, except
- *     where marked.  The library allocates nothing and keeps no mutable global
- *     state; calls on different streams touching disjoint buffers are
- *     independent.
+ *     where marked (the allocator calls take host memory).  The GPU calls
+ *     allocate nothing, device or host, and the library keeps no mutable
+ *     global state; calls on different streams touching disjoint buffers are
+ *     independent.  The only host allocation is a KV block allocator's own
+ *     state, made by fe_kv_allocator_create and freed by
+ *     fe_kv_allocator_destroy.
  *   - Every call is asynchronous on `stream` (0 = the null stream).  One
  *     stream orders an append before the attention that reads it.
  *   - Tensor pointers must be 16-byte aligned (FE_ERR_INVALID_ARG otherwise);

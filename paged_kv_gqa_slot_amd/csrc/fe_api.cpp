@@ -43,6 +43,10 @@ int check_heads(const char* func, int Hq, int Hkv, int D, int BS) {
 // The kernels move 16-byte units; every tensor pointer must allow that.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A launch's work-items (workgroups x threads) must stay below 2^32.
+bool launch_fits(double workgroups, int threads) { return workgroups * threads < 4294967296.0; }
+constexpr const char* kTooLarge = "sizes need a launch of 2^32 or more work-items";
+
 }  // namespace
 
 extern "C" {
@@ -76,6 +80,7 @@ int fe_paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot
     if (!k_new || !v_new || !slot_mapping) return fail(FE_ERR_NULL, fn, "k_new, v_new, slot_mapping must not be NULL");
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
       return fail(FE_ERR_INVALID_ARG, fn, "k_new, v_new, k_cache, v_cache must be 16-byte aligned");
+    if (!launch_fits(static_cast<double>(T) * Hkv * 32 / 256, 256)) return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     const hipError_t e = fe::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, T, num_blocks, Hkv, stream);
     return e == hipSuccess ? FE_OK : hip_fail(e, fn);
   } catch (...) {
@@ -118,6 +123,9 @@ int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cach
     if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
       return fail(FE_ERR_WORKSPACE, fn, "workspace missing or smaller than fe_paged_gqa_decode_workspace_size()");
     if (B == 0) return FE_OK;
+    if (!launch_fits(static_cast<double>(B) * plan.partitions * Hkv, 256) ||
+        !launch_fits(static_cast<double>(B) * Hq / 4, 256))
+      return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     fe::DecodeArgs a{out, lse, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv,
                      num_blocks, max_context_len, scale, plan, workspace};
     const hipError_t e = fe::launch_decode(a, stream);
@@ -145,6 +153,7 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
                   "out, q, query_start_loc, k_cache, v_cache, block_tables, context_lens must not be NULL");
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
       return fail(FE_ERR_INVALID_ARG, fn, "out, q, k_cache, v_cache must be 16-byte aligned");
+    if (!launch_fits((max_q_len / 32.0 + 1) * Hkv * B, 512)) return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     fe::PrefillArgs a{out, lse, q, query_start_loc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                       B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale};
     const hipError_t e = fe::launch_prefill(a, stream);
@@ -189,6 +198,8 @@ int fe_paged_gqa_mixed(void* out, float* lse, const void* q, const int32_t* quer
                   "out, q, query_start_loc, k_cache, v_cache, block_tables, context_lens must not be NULL");
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
       return fail(FE_ERR_INVALID_ARG, fn, "out, q, k_cache, v_cache, workspace must be 16-byte aligned");
+    if (!launch_fits((max_q_len / 32.0 + 1) * Hkv * B + static_cast<double>(num_decode) * plan.partitions * Hkv, 512))
+      return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     fe::MixedArgs a{{out, lse, q, query_start_loc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale},
                     num_decode, plan, workspace};
@@ -217,6 +228,8 @@ int fe_qk_norm_rope_append(void* q_out, const void* q, const void* k, const void
     if (!aligned16(q_out) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_norm_w) ||
         !aligned16(k_norm_w) || !aligned16(cos_sin) || !aligned16(k_cache) || !aligned16(v_cache))
       return fail(FE_ERR_INVALID_ARG, fn, "q_out, q, k, v, the norm weights, cos_sin and the pools must be 16-byte aligned");
+    if (!launch_fits(static_cast<double>(T) * (Hq + 2.0 * Hkv) / 16 + 1, 256))
+      return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     const fe::NormRopeArgs a{q_out, q, k, v, q_norm_w, k_norm_w, cos_sin, max_pos, positions, slot_mapping, k_cache,
                              v_cache, T, Hq, Hkv, num_blocks, eps};
     const hipError_t e = fe::launch_qk_norm_rope(a, stream);
@@ -243,6 +256,7 @@ int fe_sampler_softmax_argmax(float* probs, float* lse, int32_t* argmax, const v
     if (!aligned16(logits) || !aligned16(probs))
       return fail(FE_ERR_INVALID_ARG, fn, "logits and probs must be 16-byte aligned");
     const fe::SamplerPlan plan = fe::plan_sampler(B, V);
+    if (!launch_fits(static_cast<double>(B) * plan.chunks, 256)) return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     if (!workspace || workspace_bytes < plan.workspace_bytes)
       return fail(FE_ERR_WORKSPACE, fn, "workspace missing or smaller than fe_sampler_workspace_size()");
     const fe::SamplerArgs a{probs, lse, argmax, logits, inv_temperature, B, V, plan, workspace};

@@ -249,3 +249,11 @@ def test_sampler_argument_errors(lib):
     assert smp(lib, x=P + 2) == INVALID
     assert smp(lib, B=0, x=None, am=None) == OK
     assert lib.fe_sampler_workspace_size(4, 1001) == ctypes.c_size_t(-1).value
+
+
+def test_oversized_launches_rejected(lib):
+    """Sizes whose launch would reach 2^32 work-items are refused on the host."""
+    assert app(lib, T=1 << 30, NB=1 << 20) == UNSUPPORTED
+    assert pre(lib, mql=1 << 30, B=1 << 10, tq=1 << 30) == UNSUPPORTED
+    assert nr(lib, T=1 << 28) == UNSUPPORTED
+    assert "2^32" in fe.fe_last_error()
