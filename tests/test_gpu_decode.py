@@ -69,7 +69,7 @@ def test_append_zero_tokens_is_noop(dev):
 
 # -- decode: small cases spanning tiles, ragged tails and edge cases ------------
 
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("poison", ["nan", "large"])
 def test_decode_small(dev, G, poison):
     lens = [1, 15, 16, 17, 100, 257, 0, 33]

@@ -41,7 +41,7 @@ def run_mixed(w, dev, parts=(0,), label="", rows=None):
     return dw
 
 
-@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("poison", ["nan", "large"])
 def test_mixed_small(dev, G, poison):
     # decode rows: empty, one token, a partial block, a block boundary, several

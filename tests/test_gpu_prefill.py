@@ -44,7 +44,7 @@ def run_prefill(w, dev, label, rows=None, lens_override=None):
     return dw, out, lse
 
 
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("poison", ["nan", "large"])
 def test_prefill_small(dev, G, poison):
     chunks = [1, 31, 33, 100]
@@ -80,7 +80,7 @@ def _ragged(spec, lens, chunks, seed, poison):
                            layers=[lay])
 
 
-@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("G", [1, 3, 4, 6, 8])
 def test_prefill_tile_counts(dev, G):
     """Key ranges of 1 to 18 64-key tiles (odd and even counts, so the two
     wave groups that split the keys get equal or unequal shares, or one gets
@@ -98,6 +98,31 @@ def test_prefill_long_key_range(dev, G, lens):
     list of staged block ids is reloaded mid-sequence."""
     w = inputs.custom("prefill", 2, 2 * G, 2, lens, 500 + G, append=64, chunk=64, poison="nan")
     run_prefill(w, dev, f"long key range G={G}")
+
+
+@pytest.mark.parametrize("G", [2, 4])
+def test_prefill_zero_length_chunks(dev, G):
+    """Sequences with an empty chunk (query_start_loc repeats) sit between
+    non-empty ones: they own no rows, and every other row is unaffected."""
+    lens = [40, 33, 100, 16, 70]
+    chunks = [5, 0, 40, 0, 1]
+    spec = inputs.Spec("prefill_ragged", "prefill", len(lens), 2 * G, 2, min(lens), max(lens), append=0, chunk=0)
+    w = _ragged(spec, lens, chunks, 600 + G, "nan")
+    run_prefill(w, dev, f"zero-length chunks G={G}")
+
+
+def test_prefill_all_chunks_empty_is_noop(dev):
+    """Every chunk empty (total_q = 0, max_q_len = 0): nothing is launched or written."""
+    kc = torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    q = torch.zeros(0, 8, 128, dtype=torch.bfloat16, device=dev)
+    out = torch.zeros(0, 8, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros(0, 8, dtype=torch.float32, device=dev)
+    qsl = torch.zeros(3, dtype=torch.int32, device=dev)
+    bt = torch.zeros(2, 4, dtype=torch.int32, device=dev)
+    lens = torch.tensor([20, 0], dtype=torch.int32, device=dev)
+    fe.fe_paged_gqa_prefill_chunk(out, lse, q, qsl, kc, vc, bt, lens, 0, 64, 0.088)
+    torch.cuda.synchronize()
 
 
 def test_prefill_negative_scale(dev):
