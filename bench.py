@@ -36,6 +36,31 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA peak
 DEFAULT_WORKLOAD = "qwen3_4b_b64_ctx1024-8192"
 
 
+def spread(per_ms):
+    """p10 / p50 / p90 of sorted per-launch times (ms)."""
+    n = len(per_ms)
+    pick = lambda q: per_ms[min(n - 1, int(q * (n - 1) + 0.5))]
+    return {"p10_ms": round(pick(0.1), 5), "p50_ms": round(pick(0.5), 5), "p90_ms": round(pick(0.9), 5)}
+
+
+def streaming_read_ceiling(torch, dev):
+    """A plain streaming read on this GPU, measured in the same run: torch's
+    int64 sum over 4 GiB (the fastest of torch's full reductions here).  A
+    secondary reference beside the 8 TB/s peak; non-temporal loads go further."""
+    x = torch.ones(1 << 29, dtype=torch.int64, device=dev)
+    x.sum()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        x.sum()
+    b.record()
+    torch.cuda.synchronize()
+    gbs = x.numel() * 8 / (a.elapsed_time(b) / 5 * 1e-3) / 1e9
+    del x
+    return {"GBps": round(gbs, 1), "method": "torch int64 sum over 4 GiB, same run"}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -173,19 +198,23 @@ def cpu_baseline(w, budget_s: float):
             if el >= budget_s or reps >= 50:
                 break
         per = el / reps
+        t0 = time.perf_counter()
+        oracle.decode(lay.q, rk, rv, w.block_tables, w.context_lens, w.scale, nthreads=1)
+        one = time.perf_counter() - t0
         return {"value": round(decode_bytes(w) / per / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
                 "sample": f"fp64 oracle decode over the full workload ({w.kv_tokens} KV tokens x {w.Hkv} KV heads), "
                           f"{reps} repetitions, {per * 1e3:.1f} ms each; append not included",
-                "kv_tokens_per_s": round(w.kv_tokens / per, 1)}
+                "kv_tokens_per_s": round(w.kv_tokens / per, 1), "nproc": os.cpu_count(),
+                "single_thread_value": round(decode_bytes(w) / one / 1e9, 3)}
     # prefill: a bounded, evenly spread sample of packed rows, scaled to the
     # whole chunk (a probe of 32 rows sizes the sample to the time budget)
     total_q = lay.q.shape[0]
 
-    def run(n):
+    def run(n, nthreads=threads):
         rows = [int(round(i * (total_q - 1) / max(1, n - 1))) for i in range(n)] if n > 1 else [0]
         t0 = time.perf_counter()
         oracle.prefill_chunk(lay.q, w.query_start_loc, rk, rv, w.block_tables, w.context_lens, w.scale, rows=rows,
-                             nthreads=threads)
+                             nthreads=nthreads)
         return rows, time.perf_counter() - t0
 
     rows, el = run(min(total_q, 32))
@@ -193,14 +222,18 @@ def cpu_baseline(w, budget_s: float):
     if n > len(rows):
         rows, el = run(n)
     flops = sum(prefill_row_flops(w, r) for r in rows)
+    rows1, el1 = run(min(total_q, 16), nthreads=1)
+    single = sum(prefill_row_flops(w, r) for r in rows1) / el1
     if w.spec.kind == "mixed":  # the whole step's time, scaled from the sample by flops
         total = sum(prefill_row_flops(w, r) for r in range(total_q))
         return {"value": round(total / (flops / el) * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
                 "sample": f"fp64 oracle on {len(rows)} of {total_q} query rows (decode rows and prefill chunks) "
-                          f"({el:.1f} s), scaled to the whole step by flops; append not included"}
+                          f"({el:.1f} s), scaled to the whole step by flops; append not included",
+                "nproc": os.cpu_count(), "single_thread_value": round(total / single * 1e6, 1)}
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle prefill on {len(rows)} of {total_q} query rows spread over the chunk "
-                      f"({el:.1f} s); flops counted for those rows"}
+                      f"({el:.1f} s); flops counted for those rows",
+            "nproc": os.cpu_count(), "single_thread_value": round(single / 1e12, 6)}
 
 
 def calibrate_copies(args, torch, dev):
@@ -265,7 +298,10 @@ def bench_norm_rope(args, w, fe, inputs, torch, dev):
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"norm_rope:{w.spec.name}", "norm_rope", 0),
             "kernel": "fe_qk_norm_rope_append (qk_norm_rope_kernel)", "per_launch_bytes": nbytes,
-            "avg_ms": round(avg, 5), "median_ms": round(per[len(per) // 2], 5)}
+            "avg_ms": round(avg, 5), "median_ms": round(per[len(per) // 2], 5), **spread(per)}
+    ceil = streaming_read_ceiling(torch, dev)
+    roof["streaming_read_ceiling"] = ceil
+    roof["frac_of_streaming_ceiling"] = round(achieved / ceil["GBps"], 4)
     calibrate_copies(args, torch, dev)
     cpu = None
     if not args.no_cpu_baseline:
@@ -330,7 +366,11 @@ def bench_sampler(args, fe, inputs, torch, dev):
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"sampler:qwen3_vocab{V}_b{B}", "sampler", 0),
             "kernel": "fe_sampler_softmax_argmax (sampler_partial_kernel + sampler_write_kernel)",
-            "per_launch_bytes": nbytes, "avg_ms": round(avg, 5), "median_ms": round(per[len(per) // 2], 5)}
+            "per_launch_bytes": nbytes, "avg_ms": round(avg, 5), "median_ms": round(per[len(per) // 2], 5),
+            **spread(per)}
+    ceil = streaming_read_ceiling(torch, dev)
+    roof["streaming_read_ceiling"] = ceil
+    roof["frac_of_streaming_ceiling"] = round(achieved / ceil["GBps"], 4)
     calibrate_copies(args, torch, dev)
     cpu = None
     if not args.no_cpu_baseline:
@@ -492,6 +532,24 @@ def main():
     att_ms = sorted(a.elapsed_time(b) for a, b in evs)
     att_avg_ms = sum(att_ms) / len(att_ms) / len(L)
     att_med_ms = att_ms[len(att_ms) // 2] / len(L)
+    att_spread = spread([t / len(L) for t in att_ms])
+    # cold: a 1 GiB scrub write between the append and the timed attention
+    # call, so nothing of the workload is left in the 256 MB last-level cache
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(min(args.steps, 20))]
+    for i, (a, b) in enumerate(cold):
+        for x in L:
+            if do_append:
+                fe.fe_paged_kv_append(x["kn"], x["vn"], slots, x["kc"], x["vc"])
+        scrub.fill_(float(i))
+        a.record(stream)
+        for x in L:
+            attend(x)
+        b.record(stream)
+    torch.cuda.synchronize()
+    del scrub
+    cold_ms = sorted(a.elapsed_time(b) for a, b in cold)
+    cold_med_ms = cold_ms[len(cold_ms) // 2] / len(L)
 
     nl = len(L)
     if is_decode:
@@ -504,7 +562,11 @@ def main():
                 "traffic": measured_traffic(spec.name, "decode", P),
                 "kernel": "fe_paged_gqa_decode (gqa_decode_partition_kernel + gqa_decode_merge_kernel)"
                           if P > 1 else "fe_paged_gqa_decode (gqa_decode_partition_kernel)",
-                "per_launch_bytes": att_bytes, "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5)}
+                "per_launch_bytes": att_bytes, "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5),
+                **att_spread, "cold_median_ms": round(cold_med_ms, 5)}
+        ceil = streaming_read_ceiling(torch, dev)
+        roof["streaming_read_ceiling"] = ceil
+        roof["frac_of_streaming_ceiling"] = round(achieved / ceil["GBps"], 4)
         metric = "paged GQA decode achieved HBM GB/s (% of peak) + KV tokens/s, Qwen3-4B shape"
         unit = "GB/s"
         extra = {"pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -523,7 +585,7 @@ def main():
                 "kernel": "fe_paged_gqa_mixed (gqa_mixed_kernel)", "decode_rows_bytes": dec_bytes,
                 "prefill_flops": flops, "hbm_bound_us": round(t_hbm, 2), "mfma_bound_us": round(t_mfma, 2),
                 "separate_calls_us": round(sep_us, 2), "avg_ms": round(att_avg_ms, 5),
-                "median_ms": round(att_med_ms, 5)}
+                "median_ms": round(att_med_ms, 5), **att_spread, "cold_median_ms": round(cold_med_ms, 5)}
         metric = "mixed decode+prefill step, one launch, microseconds per step, Qwen3-4B shape"
         unit = "us"
         extra = {}
@@ -535,7 +597,8 @@ def main():
                 "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
                 "traffic": measured_traffic(spec.name, "prefill", 0),
                 "kernel": "fe_paged_gqa_prefill_chunk (gqa_prefill_chunk_kernel)", "per_launch_flops": flops,
-                "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5)}
+                "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5), **att_spread,
+                "cold_median_ms": round(cold_med_ms, 5)}
         metric = "paged GQA chunked-prefill TFLOP/s (% of bf16 MFMA peak), Qwen3-4B shape"
         unit = "TFLOP/s"
         extra = {}
