@@ -522,6 +522,16 @@ MUTANTS = {
     "temperature_ignored": [("const double s = inv_temp ? static_cast<double>(inv_temp[b]) : 1.0;", "const double s = 1.0;")],
     "sampler_lse_missing_max": [("lse[b] = m + std::log(Z);", "lse[b] = std::log(Z);")],
     "sampler_probs_unnormalised": [("std::exp(s * widen_bf16(x[i]) - m) / Z;", "std::exp(s * widen_bf16(x[i]) - m);")],
+    "softmax_sum_skips_first_token": [("  double Z = 0.0;\n  for (int t = t0; t < t1; ++t) {\n    s[t - t0] = std::exp",
+                                       "  double Z = 0.0;\n  for (int t = t0; t < t1; ++t) {\n    if (t == t0) { s[0] = std::exp(s[0] - m); continue; }\n    s[t - t0] = std::exp")],
+    "value_row_one_token_late": [("const uint16_t* v = c.v + c.offset(t, g);",
+                                  "const uint16_t* v = c.v + c.offset(t + 1 < t1 ? t + 1 : t, g);")],
+    "prefill_top_left_alignment": [("const int pos = context_lens[b] - C + (r - query_start_loc[b]);",
+                                    "const int pos = r - query_start_loc[b];")],
+    "append_skips_v": [("        v_cache[dst + d] = v_new[src + d];\n", "")],
+    "decode_reads_head0_query": [("attend(out + row * D, lse + row, q + row * D, c, h / G, 0, context_lens[b], scale);",
+                                  "attend(out + row * D, lse + row, q + (row - h) * D, c, h / G, 0, context_lens[b], scale);")],
+    "sampler_lse_base2": [("lse[b] = m + std::log(Z);", "lse[b] = m + std::log2(Z);")],
 }
 
 
