@@ -58,18 +58,38 @@ __global__ __launch_bounds__(256) void gqa_decode_merge_kernel(const float* __re
   const int nblk = (L + kBlockSize - 1) / kBlockSize;
   const int np = (nblk + part_blocks - 1) / part_blocks;
   const float* lp = lse_part + static_cast<size_t>(row) * P;
-  float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, lp[i]);
-  float z = 0.f, a0 = 0.f, a1 = 0.f;
-  if (M > -INFINITY) {
-    const float2* op = reinterpret_cast<const float2*>(o_part + static_cast<size_t>(row) * P * kHeadDim) + lane;
-    for (int i = 0; i < np; ++i) {
-      const float w = fast_exp2((lp[i] - M) * kLog2e);
-      const float2 v = op[static_cast<size_t>(i) * (kHeadDim / 2)];
-      z += w;
-      a0 = fmaf(w, v.x, a0);
-      a1 = fmaf(w, v.y, a1);
+  const float2* op = reinterpret_cast<const float2*>(o_part + static_cast<size_t>(row) * P * kHeadDim) + lane;
+  // Partitions in chunks of kMergeChunk: every load of a chunk (its LSEs and
+  // this lane's partial words) is issued at once, so a row of up to
+  // kMergeChunk partitions costs one memory round trip; chunks after the
+  // first rescale the running sums to the new maximum.
+  constexpr int kMergeChunk = 16;
+  float M = -INFINITY, z = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int i0 = 0; i0 < np; i0 += kMergeChunk) {
+    float lv[kMergeChunk];
+    float2 ov[kMergeChunk];
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) {
+      const int i = i0 + k;
+      lv[k] = i < np ? lp[i] : -INFINITY;
+      ov[k] = i < np ? op[static_cast<size_t>(i) * (kHeadDim / 2)] : make_float2(0.f, 0.f);
     }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) Mc = fmaxf(Mc, lv[k]);
+    if (!(Mc > -INFINITY)) continue;  // every partition so far is empty
+    const float f = fast_exp2((M - Mc) * kLog2e);  // 0 while nothing was summed
+    z *= f;
+    a0 *= f;
+    a1 *= f;
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k) {
+      const float w = fast_exp2((lv[k] - Mc) * kLog2e);
+      z += w;
+      a0 = fmaf(w, ov[k].x, a0);
+      a1 = fmaf(w, ov[k].y, a1);
+    }
+    M = Mc;
   }
   const bool empty = !(z > 0.f);
   reinterpret_cast<uint32_t*>(out + static_cast<size_t>(row) * kHeadDim)[lane] =
