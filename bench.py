@@ -88,7 +88,7 @@ def prefill_flops(w, first: int = 0) -> int:
         if b < first:
             continue
         C = qsl[b + 1] - qsl[b]
-        tot += sum(L - C + i + 1 for i in range(C))
+        tot += sum(max(0, L - C + i + 1) for i in range(C))  # a row before the context sees no key
     return tot * w.Hq * 4 * 128
 
 
@@ -178,7 +178,7 @@ def prefill_row_flops(w, r: int) -> int:
     for b, L in enumerate(w.context_lens.tolist()):
         if qsl[b] <= r < qsl[b + 1]:
             C = qsl[b + 1] - qsl[b]
-            return (L - C + (r - qsl[b]) + 1) * w.Hq * 4 * 128
+            return max(0, L - C + (r - qsl[b]) + 1) * w.Hq * 4 * 128
     return 0
 
 
