@@ -519,8 +519,10 @@ def main():
         graph_ms = None
 
     # per-kernel timing of the attention call (the dominant kernel), same stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for z, a, b in evs:
+        z.record(stream)
         for x in L:
             if do_append:
                 fe.fe_paged_kv_append(x["kn"], x["vn"], slots, x["kc"], x["vc"])
@@ -529,7 +531,8 @@ def main():
             attend(x)
         b.record(stream)
     torch.cuda.synchronize()
-    att_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    att_ms = sorted(a.elapsed_time(b) for _, a, b in evs)
+    append_ms = sorted(z.elapsed_time(a) for z, a, _ in evs) if do_append else None
     att_avg_ms = sum(att_ms) / len(att_ms) / len(L)
     att_med_ms = att_ms[len(att_ms) // 2] / len(L)
     att_spread = spread([t / len(L) for t in att_ms])
@@ -610,6 +613,10 @@ def main():
         log("timing the CPU oracle baseline ...")
         cpu = cpu_baseline(w, args.cpu_budget)
 
+    if append_ms:
+        extra["append_median_ms"] = round(append_ms[len(append_ms) // 2] / nl, 5)
+        extra["append_plus_attention_median_ms"] = round(
+            sorted(z.elapsed_time(b) for z, _, b in evs)[len(evs) // 2] / nl, 5)
     cfg = {"workload": spec.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": 128,
            "block_size": 16, "layers": nl, "kv_tokens": w.kv_tokens, "max_context_len": mcl,
            "append_tokens_per_step": int(slots.numel()) * nl, "num_partitions": P, "seed": w.seed,
