@@ -385,12 +385,20 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     __syncthreads();
   };
 
-  if (S::KS == 2 && grp == 1) __syncthreads();  // run one phase behind group 0
+  // Prologue.  Q and the block ids of the first 64 tiles arrive in one
+  // memory round trip, settled on every path here so that no later barrier
+  // waits on memory; each key group then stages its first tile and issues
+  // the second tile's loads before the barriers, so the two groups' first
+  // HBM round trips overlap.  Group 1 then takes one extra barrier, which
+  // puts it one phase behind group 0.
+  load_ids(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   if (n_g > 0) {
     fetch(t_first);
     stash(B0{});
   }
   if (n_g > 1) fetch(t_first + 1);
+  if (S::KS == 2 && grp == 1) __syncthreads();
   __syncthreads();
   if (n_g > 0) step(B0{}, std::false_type{}, 0);  // the first tile has no PV of a previous one
   int i = 1;
