@@ -173,6 +173,28 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
                                int max_context_len, float scale, hipStream_t stream);
 
 /*
+ * fe_paged_gqa_prefill_chunk with the kernel's tile shape chosen by the
+ * caller; every other argument, the result's definition and the errors are
+ * the same.
+ *   key_groups     0 = automatic (what fe_paged_gqa_prefill_chunk does);
+ *                  1 = each workgroup walks its keys with one group of waves
+ *                  (two workgroups fit on a compute unit);
+ *                  2 = two wave groups split the keys and merge by
+ *                  log-sum-exp (one workgroup per compute unit); valid only
+ *                  for Hq/Hkv <= 4, else FE_ERR_UNSUPPORTED.
+ *                  Other values: FE_ERR_INVALID_ARG.
+ * The automatic choice takes 2 when the launch has at most one workgroup
+ * per compute unit and 1 otherwise.  The shapes differ only in the order
+ * of fp32 additions, so results agree within rounding, not bit for bit.
+ * Source: as fe_paged_gqa_prefill_chunk.
+ */
+int fe_paged_gqa_prefill_chunk_ex(void* out, float* lse, const void* q, const int32_t* query_start_loc,
+                                  const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* context_lens, int B, int total_q,
+                                  int max_q_len, int Hq, int Hkv, int D, int BS, int num_blocks,
+                                  int max_context_len, float scale, int key_groups, hipStream_t stream);
+
+/*
  * Bytes of device workspace fe_paged_gqa_mixed needs for these sizes
  * (num_partitions 0 = automatic).  Host-only; 0 when no decode sequence is
  * split, (size_t)-1 for invalid sizes.

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     fe_paged_gqa_mixed,
     fe_paged_gqa_mixed_workspace_size,
     fe_paged_gqa_prefill_chunk,
+    fe_paged_gqa_prefill_chunk_ex,
     fe_paged_kv_append,
     fe_qk_norm_rope_append,
     fe_sampler_softmax_argmax,

@@ -51,6 +51,8 @@ def load_library():
     lib.fe_paged_gqa_decode.restype = I
     lib.fe_paged_gqa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, P]
     lib.fe_paged_gqa_prefill_chunk.restype = I
+    lib.fe_paged_gqa_prefill_chunk_ex.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, I, P]
+    lib.fe_paged_gqa_prefill_chunk_ex.restype = I
     lib.fe_paged_gqa_mixed_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.fe_paged_gqa_mixed_workspace_size.restype = Z
     lib.fe_paged_gqa_mixed.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, F, I, P, Z, P]
@@ -180,6 +182,23 @@ def fe_paged_gqa_prefill_chunk(out, lse, q, query_start_loc, k_cache, v_cache, b
         block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens", 1), B, total_q, int(max_q_len),
         Hq, Hkv, D, BS, NB, int(max_context_len), float(scale), _stream(stream))
     _check(rc, "fe_paged_gqa_prefill_chunk")
+
+
+def fe_paged_gqa_prefill_chunk_ex(out, lse, q, query_start_loc, k_cache, v_cache, block_tables, context_lens,
+                                  max_q_len: int, max_context_len: int, scale: float, key_groups: int,
+                                  stream=None) -> None:
+    """fe_paged_gqa_prefill_chunk with the tile shape chosen by the caller
+    (key_groups 0 automatic, 1 or 2 wave groups per workgroup)."""
+    total_q, Hq, D = q.shape
+    NB, Hkv, BS, _ = k_cache.shape
+    B = context_lens.shape[0]
+    rc = load_library().fe_paged_gqa_prefill_chunk_ex(
+        _dev(out, torch.bfloat16, "out", 3), _dev(lse, torch.float32, "lse", 2), _dev(q, torch.bfloat16, "q", 3),
+        _dev(query_start_loc, torch.int32, "query_start_loc", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
+        _dev(v_cache, torch.bfloat16, "v_cache", 4), _dev(block_tables, torch.int32, "block_tables", 2),
+        block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens", 1), B, total_q, int(max_q_len),
+        Hq, Hkv, D, BS, NB, int(max_context_len), float(scale), int(key_groups), _stream(stream))
+    _check(rc, "fe_paged_gqa_prefill_chunk_ex")
 
 
 def fe_paged_gqa_mixed_workspace_size(num_decode, Hq, Hkv, D, max_context_len, num_partitions=0) -> int:

@@ -135,18 +135,21 @@ int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cach
   }
 }
 
-int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32_t* query_start_loc,
-                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                               int max_blocks_per_seq, const int32_t* context_lens, int B, int total_q, int max_q_len,
-                               int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale,
-                               hipStream_t stream) {
-  static const char* fn = "fe_paged_gqa_prefill_chunk";
+namespace {
+
+int prefill_chunk(const char* fn, void* out, float* lse, const void* q, const int32_t* query_start_loc,
+                  const void* k_cache, const void* v_cache, const int32_t* block_tables, int max_blocks_per_seq,
+                  const int32_t* context_lens, int B, int total_q, int max_q_len, int Hq, int Hkv, int D, int BS,
+                  int num_blocks, int max_context_len, float scale, int key_groups, hipStream_t stream) {
   try {
+    if (key_groups < 0 || key_groups > 2) return fail(FE_ERR_INVALID_ARG, fn, "key_groups must be 0, 1 or 2");
     if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
       return fail(FE_ERR_INVALID_ARG, fn,
                   "B, total_q, max_q_len, max_context_len must be >= 0; num_blocks, max_blocks_per_seq positive");
     if (int rc = check_heads(fn, Hq, Hkv, D, BS)) return rc;
     if (!isfinite(scale)) return fail(FE_ERR_INVALID_ARG, fn, "scale must be finite");
+    if (key_groups == 2 && !fe::prefill_two_key_groups_supported(Hq / Hkv))
+      return fail(FE_ERR_UNSUPPORTED, fn, "key_groups 2 needs Hq/Hkv <= 4");
     if (B == 0 || total_q == 0) return FE_OK;
     if (!out || !q || !query_start_loc || !k_cache || !v_cache || !block_tables || !context_lens)
       return fail(FE_ERR_NULL, fn,
@@ -155,12 +158,34 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
       return fail(FE_ERR_INVALID_ARG, fn, "out, q, k_cache, v_cache must be 16-byte aligned");
     if (!launch_fits((max_q_len / 32.0 + 1) * Hkv * B, 512)) return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     fe::PrefillArgs a{out, lse, q, query_start_loc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
-                      B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale};
+                      B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale, key_groups};
     const hipError_t e = fe::launch_prefill(a, stream);
     return e == hipSuccess ? FE_OK : hip_fail(e, fn);
   } catch (...) {
     return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
   }
+}
+
+}  // namespace
+
+int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32_t* query_start_loc,
+                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                               int max_blocks_per_seq, const int32_t* context_lens, int B, int total_q, int max_q_len,
+                               int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale,
+                               hipStream_t stream) {
+  return prefill_chunk("fe_paged_gqa_prefill_chunk", out, lse, q, query_start_loc, k_cache, v_cache, block_tables,
+                       max_blocks_per_seq, context_lens, B, total_q, max_q_len, Hq, Hkv, D, BS, num_blocks,
+                       max_context_len, scale, 0, stream);
+}
+
+int fe_paged_gqa_prefill_chunk_ex(void* out, float* lse, const void* q, const int32_t* query_start_loc,
+                                  const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* context_lens, int B, int total_q,
+                                  int max_q_len, int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len,
+                                  float scale, int key_groups, hipStream_t stream) {
+  return prefill_chunk("fe_paged_gqa_prefill_chunk_ex", out, lse, q, query_start_loc, k_cache, v_cache,
+                       block_tables, max_blocks_per_seq, context_lens, B, total_q, max_q_len, Hq, Hkv, D, BS,
+                       num_blocks, max_context_len, scale, key_groups, stream);
 }
 
 size_t fe_paged_gqa_mixed_workspace_size(int num_decode, int Hq, int Hkv, int D, int max_context_len,

@@ -2,7 +2,8 @@
 // README, "What it implements": restricted prefill lab, and "Scheduling":
 // token-budgeted batching that cuts prompts into chunks; "Make the Engine
 // Talk" section 1.2: the prefill pass that primes the cache).  One workgroup
-// per (sequence, KV head, query tile) runs the tile of prefill_body.h.
+// per (sequence, KV head, query tile) runs the tile of prefill_body.h, with
+// its keys split over two wave groups or handled by one (launch_g below).
 #include <math.h>
 
 #include "prefill_body.h"
@@ -12,41 +13,70 @@ namespace {
 
 using namespace pre;
 
-template <int G>
-__global__ __launch_bounds__(Shape<G>::kThreads) void gqa_prefill_chunk_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[Shape<G>::kLdsBytes];
+constexpr int kCuCount = 256;
+
+// One kernel per (group size, key groups).  Both shapes use at most 256
+// VGPRs, two waves per SIMD: one workgroup of two key groups per CU, or two
+// single-group workgroups per CU (each takes half the LDS).
+template <int G, int KSel>
+__global__ __launch_bounds__((Shape<G, KSel>::kThreads)) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+gqa_prefill_chunk_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Shape<G, KSel>::kLdsBytes];
   // Workgroups are dispatched round-robin over the 8 XCDs (id mod 8).  The
   // query tile is the slowest-varying index, so all tiles of one (sequence,
   // KV head) pair share an XCD and read its K/V through one L2.
   const int pairs = p.B * p.Hkv;
   const int pair = blockIdx.x % pairs;
-  prefill_tile<G>(p, lds, blockIdx.x / pairs, pair / p.Hkv, pair % p.Hkv);
+  prefill_tile<G, KSel>(p, lds, blockIdx.x / pairs, pair / p.Hkv, pair % p.Hkv);
 }
 
+template <int G, int KSel>
+hipError_t launch_shape(PrefillParams prm, long grid, hipStream_t stream) {
+  void* args[] = {&prm};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gqa_prefill_chunk_kernel<G, KSel>),
+                         dim3(static_cast<unsigned>(grid)), dim3(Shape<G, KSel>::kThreads), args, 0, stream);
+}
+
+// Key groups per workgroup.  Two groups (8 waves, one workgroup per CU) pair
+// each SIMD's MFMA phase with the other group's softmax phase; with at most
+// one workgroup per CU that is the faster shape.  A larger grid runs
+// workgroups back to back on each CU, and there one group per workgroup
+// (two resident workgroups per CU) wins: one workgroup's prologue, epilogue
+// and tail overlap the other's key loop.  Measured on MI355X at Hq/Hkv = 4:
+// 256 workgroups, two groups 12% faster; 384 to 512, one group 2-5% faster;
+// 768 to 4096, one group 12-15% faster.
 template <int G>
-hipError_t launch_g(const PrefillParams& prm, hipStream_t stream) {
+hipError_t launch_g(const PrefillArgs& a, const PrefillParams& prm, hipStream_t stream) {
   PrefillParams copy = prm;
   copy.qtiles = (prm.max_q_len + Shape<G>::QT - 1) / Shape<G>::QT;
   const long grid = static_cast<long>(copy.qtiles) * prm.Hkv * prm.B;
   if (grid == 0) return hipSuccess;
-  void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gqa_prefill_chunk_kernel<G>), dim3(static_cast<unsigned>(grid)),
-                         dim3(Shape<G>::kThreads), args, 0, stream);
+  if constexpr (Shape<G>::KS == 2) {
+    const int ks = a.key_groups != 0 ? a.key_groups : (grid > kCuCount ? 1 : 2);
+    if (ks == 1) return launch_shape<G, 1>(copy, grid, stream);
+  } else {
+    if (a.key_groups == 2) return hipErrorInvalidValue;
+  }
+  return launch_shape<G, 0>(copy, grid, stream);
 }
 
 }  // namespace
 
+static_assert(Shape<1>::KS == 2 && Shape<3>::KS == 2 && Shape<4>::KS == 2 && Shape<5>::KS == 1,
+              "two key groups exactly for Hq/Hkv <= 4");
+bool prefill_two_key_groups_supported(int G) { return G >= 1 && G <= 4; }
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const PrefillParams prm = make_prefill_params(a);
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_g<1>(prm, stream);
-    case 2: return launch_g<2>(prm, stream);
-    case 3: return launch_g<3>(prm, stream);
-    case 4: return launch_g<4>(prm, stream);
-    case 5: return launch_g<5>(prm, stream);
-    case 6: return launch_g<6>(prm, stream);
-    case 7: return launch_g<7>(prm, stream);
-    case 8: return launch_g<8>(prm, stream);
+    case 1: return launch_g<1>(a, prm, stream);
+    case 2: return launch_g<2>(a, prm, stream);
+    case 3: return launch_g<3>(a, prm, stream);
+    case 4: return launch_g<4>(a, prm, stream);
+    case 5: return launch_g<5>(a, prm, stream);
+    case 6: return launch_g<6>(a, prm, stream);
+    case 7: return launch_g<7>(a, prm, stream);
+    case 8: return launch_g<8>(a, prm, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -78,10 +78,12 @@ struct PrefillParams {
   int negate_q;      // scale < 0: q's signs are flipped on load (exact)
 };
 
-template <int G>
+// KSel = 0 takes the default number of key groups (two when a group has at
+// most 4 waves); KSel = 1 forces one group, half the LDS of two.
+template <int G, int KSel = 0>
 struct Shape {
   static constexpr int W = (G <= 4 && 4 % G == 0) ? 4 : G;  // waves per group
-  static constexpr int KS = W <= 4 ? 2 : 1;                 // groups splitting the keys
+  static constexpr int KS = KSel != 0 ? KSel : (W <= 4 ? 2 : 1);  // groups splitting the keys
   static constexpr int QT = 32 * W / G;                     // query rows per workgroup
   static constexpr int kThreads = 64 * W * KS;
   // a 64-key tile is 4 KV blocks; wave w of a group stages blocks w, w + W, ...
@@ -92,10 +94,10 @@ struct Shape {
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // Query tile qt of sequence b against KV head g, run by the whole workgroup
-// (Shape<G>::kThreads threads); lds holds Shape<G>::kLdsBytes bytes.
-template <int G>
+// (Shape<G, KSel>::kThreads threads); lds holds Shape<G, KSel>::kLdsBytes bytes.
+template <int G, int KSel = 0>
 __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned char* lds, int qt, int b, int g) {
-  using S = Shape<G>;
+  using S = Shape<G, KSel>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave_all = uniform(tid >> 6);

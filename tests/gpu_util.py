@@ -80,15 +80,21 @@ class DeviceWorkload:
         torch.cuda.synchronize()
         return out, lse
 
-    def prefill(self, max_q_len=None):
+    def prefill(self, max_q_len=None, key_groups=None):
+        """fe_paged_gqa_prefill_chunk, or fe_paged_gqa_prefill_chunk_ex with
+        the given tile shape (key_groups 0, 1 or 2)."""
         w = self.w
         total_q = self.q.shape[0]
         out = torch.full((total_q, w.Hq, 128), float("nan"), dtype=torch.bfloat16, device=self.dev)
         lse = torch.full((total_q, w.Hq), float("nan"), dtype=torch.float32, device=self.dev)
         qsl = w.query_start_loc.tolist()
         mql = max(b - a for a, b in zip(qsl[:-1], qsl[1:])) if max_q_len is None else max_q_len
-        fe.fe_paged_gqa_prefill_chunk(out, lse, self.q, self.qsl, self.kc, self.vc, self.bt, self.lens, mql,
-                                      w.max_context_len, w.scale)
+        if key_groups is None:
+            fe.fe_paged_gqa_prefill_chunk(out, lse, self.q, self.qsl, self.kc, self.vc, self.bt, self.lens, mql,
+                                          w.max_context_len, w.scale)
+        else:
+            fe.fe_paged_gqa_prefill_chunk_ex(out, lse, self.q, self.qsl, self.kc, self.vc, self.bt, self.lens, mql,
+                                             w.max_context_len, w.scale, key_groups)
         torch.cuda.synchronize()
         return out, lse
 

@@ -138,6 +138,31 @@ def pre(lib, **kw):
                                           a["NB"], a["mcl"], a["scale"], a["stream"])
 
 
+def pre_ex(lib, key_groups, **kw):
+    a = dict(out=P, lse=None, q=P, qsl=P, k=P, v=P, bt=P, mb=8, cl=P, B=2, tq=16, mql=8, Hq=32, Hkv=8, D=128, BS=16,
+             NB=64, mcl=128, scale=0.088, stream=None)
+    a.update(kw)
+    return lib.fe_paged_gqa_prefill_chunk_ex(a["out"], a["lse"], a["q"], a["qsl"], a["k"], a["v"], a["bt"], a["mb"],
+                                             a["cl"], a["B"], a["tq"], a["mql"], a["Hq"], a["Hkv"], a["D"], a["BS"],
+                                             a["NB"], a["mcl"], a["scale"], key_groups, a["stream"])
+
+
+def test_prefill_ex_key_groups_checks(lib):
+    # checked before anything is enqueued; B = 0 makes every valid call a no-op
+    for kg in (0, 1, 2):
+        assert pre_ex(lib, kg, B=0) == OK
+    assert pre_ex(lib, 3, B=0) == INVALID
+    assert pre_ex(lib, -1, B=0) == INVALID
+    assert pre_ex(lib, 2, B=0, Hq=40, Hkv=8) == UNSUPPORTED  # two groups exist only for Hq/Hkv <= 4
+    assert pre_ex(lib, 1, B=0, Hq=64, Hkv=8) == OK
+    assert pre_ex(lib, 2, B=0, Hq=24, Hkv=8) == OK
+    # the other checks are those of fe_paged_gqa_prefill_chunk
+    assert pre_ex(lib, 1, qsl=None) == NULL
+    assert pre_ex(lib, 2, D=96) == UNSUPPORTED
+    assert pre_ex(lib, 5, B=0) == INVALID
+    assert "key_groups" in fe.fe_last_error()
+
+
 def test_prefill_argument_errors(lib):
     assert pre(lib, qsl=None) == NULL
     assert pre(lib, q=None) == NULL

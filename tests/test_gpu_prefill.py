@@ -29,13 +29,13 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run_prefill(w, dev, label, rows=None, lens_override=None):
+def run_prefill(w, dev, label, rows=None, lens_override=None, key_groups=None):
     dw = DeviceWorkload(w, dev)
     rk, rv = dw.append()
     lens = w.context_lens if lens_override is None else lens_override
     if lens_override is not None:
         dw.lens = lens_override.to(dev)
-    out, lse = dw.prefill()
+    out, lse = dw.prefill(key_groups=key_groups)
     ro, rl = oracle.prefill_chunk(dw.lay.q, w.query_start_loc, rk, rv, w.block_tables, lens, w.scale, rows=rows)
     if rows is not None:
         idx = torch.as_tensor(rows, dtype=torch.long, device=dev)
@@ -44,15 +44,29 @@ def run_prefill(w, dev, label, rows=None, lens_override=None):
     return dw, out, lse
 
 
+# Tile shapes: None is fe_paged_gqa_prefill_chunk (automatic: two key groups
+# per workgroup for Hq/Hkv <= 4 on these small grids, one above); 1 forces one
+# key group through fe_paged_gqa_prefill_chunk_ex.  Forcing one group where
+# it is already the default repeats the automatic case and is skipped.
+KEY_GROUPS = [None, 1]
+
+
+def _skip_repeat(G, kg):
+    if kg == 1 and G > 4:
+        pytest.skip("one key group is already the automatic tile for Hq/Hkv > 4")
+
+
+@pytest.mark.parametrize("kg", KEY_GROUPS)
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("poison", ["nan", "large"])
-def test_prefill_small(dev, G, poison):
+def test_prefill_small(dev, G, poison, kg):
+    _skip_repeat(G, kg)
     chunks = [1, 31, 33, 100]
     prefix = [0, 17, 130, 64]
     lens = [p + c for p, c in zip(prefix, chunks)]
     spec = inputs.Spec("prefill_ragged", "prefill", 4, 2 * G, 2, min(lens), max(lens), append=0, chunk=0)
     w = _ragged(spec, lens, chunks, 200 + G, poison)
-    run_prefill(w, dev, f"prefill G={G} {poison}")
+    run_prefill(w, dev, f"prefill G={G} {poison} key_groups={kg}", key_groups=kg)
 
 
 def _ragged(spec, lens, chunks, seed, poison):
@@ -80,35 +94,61 @@ def _ragged(spec, lens, chunks, seed, poison):
                            layers=[lay])
 
 
+@pytest.mark.parametrize("kg", KEY_GROUPS)
 @pytest.mark.parametrize("G", [1, 3, 4, 6, 8])
-def test_prefill_tile_counts(dev, G):
+def test_prefill_tile_counts(dev, G, kg):
     """Key ranges of 1 to 18 64-key tiles (odd and even counts, so the two
     wave groups that split the keys get equal or unequal shares, or one gets
     none) with chunks of 1 to 300 rows."""
     lens = [64, 65, 128, 190, 257, 1000, 1088, 700]
     chunks = [64, 1, 100, 190, 3, 300, 1, 129]
     spec = inputs.Spec("prefill_ragged", "prefill", len(lens), 2 * G, 2, min(lens), max(lens), append=0, chunk=0)
+    _skip_repeat(G, kg)
     w = _ragged(spec, lens, chunks, 400 + G, "nan")
-    run_prefill(w, dev, f"tile counts G={G}")
+    run_prefill(w, dev, f"tile counts G={G} key_groups={kg}", key_groups=kg)
 
 
+@pytest.mark.parametrize("kg", KEY_GROUPS)
 @pytest.mark.parametrize("G,lens", [(4, [9000, 8300]), (8, [4500, 4200])])
-def test_prefill_long_key_range(dev, G, lens):
+def test_prefill_long_key_range(dev, G, lens, kg):
     """More than 64 tiles of keys per wave group, so the kernel's per-wave
     list of staged block ids is reloaded mid-sequence."""
+    _skip_repeat(G, kg)
     w = inputs.custom("prefill", 2, 2 * G, 2, lens, 500 + G, append=64, chunk=64, poison="nan")
-    run_prefill(w, dev, f"long key range G={G}")
+    run_prefill(w, dev, f"long key range G={G} key_groups={kg}", key_groups=kg)
 
 
+@pytest.mark.parametrize("kg", KEY_GROUPS)
 @pytest.mark.parametrize("G", [2, 4])
-def test_prefill_zero_length_chunks(dev, G):
+def test_prefill_zero_length_chunks(dev, G, kg):
     """Sequences with an empty chunk (query_start_loc repeats) sit between
     non-empty ones: they own no rows, and every other row is unaffected."""
     lens = [40, 33, 100, 16, 70]
     chunks = [5, 0, 40, 0, 1]
     spec = inputs.Spec("prefill_ragged", "prefill", len(lens), 2 * G, 2, min(lens), max(lens), append=0, chunk=0)
     w = _ragged(spec, lens, chunks, 600 + G, "nan")
-    run_prefill(w, dev, f"zero-length chunks G={G}")
+    run_prefill(w, dev, f"zero-length chunks G={G} key_groups={kg}", key_groups=kg)
+
+
+@pytest.mark.parametrize("B,auto_groups", [(32, 2), (33, 1)])
+def test_prefill_automatic_tile_choice(dev, B, auto_groups):
+    """32-row chunks over 8 KV heads: B = 32 is a grid of 256 workgroups
+    (one per compute unit, two key groups), B = 33 one of 264 (one key group,
+    two workgroups per CU).  The automatic call reproduces the chosen shape
+    bit for bit, and both shapes match the oracle.  The two shapes add the
+    key halves in different orders, so their LSEs are not all identical."""
+    lens = [40 + (37 * b) % 260 for b in range(B)]
+    w = inputs.custom("prefill", B, 32, 8, lens, 700 + B, append=32, chunk=32, poison="nan")
+    dw = DeviceWorkload(w, dev)
+    rk, rv = dw.append()
+    auto = dw.prefill()
+    ro, rl = oracle.prefill_chunk(dw.lay.q, w.query_start_loc, rk, rv, w.block_tables, w.context_lens, w.scale)
+    res = {}
+    for kg in (1, 2):
+        res[kg] = dw.prefill(key_groups=kg)
+        assert_attention(*res[kg], ro, rl, f"B={B} key_groups={kg}")
+    assert torch.equal(res[auto_groups][0], auto[0]) and torch.equal(res[auto_groups][1], auto[1])
+    assert not torch.equal(res[1][1], res[2][1])
 
 
 def test_prefill_all_chunks_empty_is_noop(dev):
@@ -190,6 +230,15 @@ def test_prefill_golden(dev):
         assert abs(float(out[r, h, d]) - val) <= 1e-2
     for r, h, val in ex["expect_lse"]:
         assert abs(float(lse[r, h]) - val) <= 1e-3
+
+
+def test_prefill_qwen3_4b_b64_prefix1024_chunk256(dev):
+    """The 64 x (1024 + 256) step: 4096 workgroups, so the automatic call
+    runs one key group per workgroup; sampled rows cover every sequence."""
+    w = inputs.make("qwen3_4b_b64_prefix1024_chunk256", poison="nan")
+    total_q = int(w.query_start_loc[-1])
+    rows = sorted(set(list(range(0, total_q, 37)) + [0, 255, 256, total_q - 1]))
+    run_prefill(w, dev, "prefill 4b b64 prefix 1024", rows=rows)
 
 
 @pytest.mark.parametrize("seed", [5, 6])
