@@ -37,7 +37,7 @@ __device__ __forceinline__ void store_nt(void* p, uint4 w) {
 
 constexpr int kRowLanes = 16;
 constexpr int kThreads = 256;
-constexpr int kRowsPerWg = kThreads / kRowLanes;
+constexpr int kRowGroups = kThreads / kRowLanes;  // rows a workgroup holds at once
 
 struct NormRopeParams {
   uint16_t* q_out;
@@ -65,75 +65,142 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
+// One head row as this lane sees it: which token / kind / head, its slot, and
+// this lane's 16 bytes of the row.
+struct Row {
+  bool live;
+  int t, kind, head;  // kind: 0 q, 1 k, 2 v
+  int pos;            // rotary table row (q and k rows)
+  int64_t slot;
+  uint4 xw;
+  uint4 ww;               // this lane's 8 norm weights
+  float4 c0, c1, s0, s1;  // this lane's cosines and sines
+};
+
+// Each 16-lane group handles kRows rows, kRowGroups rows apart (a workgroup
+// covers kRowGroups * kRows consecutive rows, every load instruction of a
+// wave reading 4 consecutive 256-byte rows).  All of a thread's loads are
+// issued before any of them is used, so a CU keeps more bytes in flight than
+// with one row per thread, which left the launch bound by bytes in flight.
+// Measured on the 16384-token step (us): 1 row 111, 2 rows 87-88 (78 VGPRs,
+// 6 waves/SIMD), 3 rows 90, 4 rows 94-97 (136 VGPRs, 3 waves/SIMD), 8 rows
+// 105-108; capping the registers for more waves spills and runs slower.
+template <int kRows>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeParams p) {
   const int c = threadIdx.x & (kRowLanes - 1);
-  const int64_t R = static_cast<int64_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x / kRowLanes);
-  const int rows_per_tok = p.Hq + 2 * p.Hkv;
-  // Rows past the end still run the row-wide DPP reductions (on zeros) so
-  // that every lane of a row takes the same path; they store nothing.
-  const bool live = R < static_cast<int64_t>(p.T) * rows_per_tok;
-  const int t = live ? static_cast<int>(R / rows_per_tok) : 0;
-  const int r = live ? static_cast<int>(R % rows_per_tok) : 0;
-  const int kind = r < p.Hq ? 0 : (r < p.Hq + p.Hkv ? 1 : 2);  // q, k, v row
-  const int head = kind == 0 ? r : (kind == 1 ? r - p.Hq : r - p.Hq - p.Hkv);
-  const int64_t slot = live ? p.slots[t] : -1;
-  const bool slot_ok = slot >= 0 && slot < p.num_slots;
+  // 32-bit row arithmetic: the entry point keeps a launch below 2^32
+  // work-items, so there are fewer than 2^28 rows.
+  const uint32_t rows_per_tok = p.Hq + 2 * p.Hkv;
+  const uint32_t total = static_cast<uint32_t>(p.T) * rows_per_tok;
+  const uint32_t R0 = blockIdx.x * (kRowGroups * kRows) + threadIdx.x / kRowLanes;
+  const uint32_t t0 = R0 / rows_per_tok;
+  const uint32_t r0 = R0 - t0 * rows_per_tok;
 
-  const uint16_t* src = kind == 0 ? p.q + (static_cast<size_t>(t) * p.Hq + head) * kHeadDim
-                                  : (kind == 1 ? p.k : p.v) + (static_cast<size_t>(t) * p.Hkv + head) * kHeadDim;
-  const uint4 xw = live ? load_nt(reinterpret_cast<const uint4*>(src) + c) : make_uint4(0, 0, 0, 0);
-  const size_t cache_off =
-      slot_ok ? ((static_cast<size_t>(slot / kBlockSize) * p.Hkv + head) * kBlockSize + slot % kBlockSize) * kHeadDim
-              : 0;
-  if (kind == 2) {  // v: bit copy into the pool
-    if (live && slot_ok) store_nt(reinterpret_cast<uint4*>(p.v_cache + cache_off) + c, xw);
-    return;
+  // Every load below is issued unconditionally at a clamped, valid address
+  // (token 0 for rows past the end): a load under a branch makes the
+  // compiler wait for it where the paths join.  Slots and positions go
+  // first, so that the rotary-table loads, which need the position, do not
+  // wait for the row loads issued after them.
+  Row row[kRows];
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    Row& w = row[k];
+    uint32_t r = r0 + k * kRowGroups;
+    const uint32_t dt = r / rows_per_tok;
+    r -= dt * rows_per_tok;
+    // Rows past the end still run the row-wide DPP reductions so that every
+    // lane of a row takes the same path; they store nothing.
+    w.live = R0 + k * kRowGroups < total;
+    w.t = w.live ? static_cast<int>(t0 + dt) : 0;
+    w.kind = static_cast<int>(r) < p.Hq ? 0 : (static_cast<int>(r) < p.Hq + p.Hkv ? 1 : 2);
+    w.head = w.kind == 0 ? r : (w.kind == 1 ? r - p.Hq : r - p.Hq - p.Hkv);
+    w.slot = p.slots[w.t];
+    const int pos = p.positions[w.t];
+    w.pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);
+  }
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    Row& w = row[k];
+    const uint16_t* src = w.kind == 0
+                              ? p.q + (static_cast<size_t>(w.t) * p.Hq + w.head) * kHeadDim
+                              : (w.kind == 1 ? p.k : p.v) + (static_cast<size_t>(w.t) * p.Hkv + w.head) * kHeadDim;
+    w.xw = load_nt(reinterpret_cast<const uint4*>(src) + c);
+    w.ww = reinterpret_cast<const uint4*>(w.kind == 0 ? p.q_w : p.k_w)[c];
+  }
+  // keep the table-address arithmetic (which waits for the positions) after
+  // the row loads are issued
+  __builtin_amdgcn_sched_barrier(0);
+  // the rotary rows (one dependent round trip, under the row loads in flight)
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    Row& w = row[k];
+    const int d0 = 8 * (c & 7);  // angle index of this lane's first dim
+    const float4* cs = reinterpret_cast<const float4*>(p.cos_sin + static_cast<size_t>(w.pos) * kHeadDim + d0);
+    w.c0 = cs[0];
+    w.c1 = cs[1];
+    w.s0 = cs[16];  // the sines sit 64 floats further
+    w.s1 = cs[17];
   }
 
-  float x[8];
-  x[0] = bf16_lo(xw.x); x[1] = bf16_hi(xw.x);
-  x[2] = bf16_lo(xw.y); x[3] = bf16_hi(xw.y);
-  x[4] = bf16_lo(xw.z); x[5] = bf16_hi(xw.z);
-  x[6] = bf16_lo(xw.w); x[7] = bf16_hi(xw.w);
-  float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ss = fmaf(x[j], x[j], ss);
-  ss = row_sum16(ss);
-  const float inv_rms = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
+  for (int k = 0; k < kRows; ++k) {
+    const Row& w = row[k];
+    const bool slot_ok = w.kind != 0 && w.slot >= 0 && w.slot < p.num_slots;
+    const size_t cache_off =
+        slot_ok ? ((static_cast<size_t>(w.slot / kBlockSize) * p.Hkv + w.head) * kBlockSize + w.slot % kBlockSize) *
+                      kHeadDim
+                : 0;
+    if (w.kind == 2) {  // v: bit copy into the pool
+      if (w.live && slot_ok) store_nt(reinterpret_cast<uint4*>(p.v_cache + cache_off) + c, w.xw);
+      continue;
+    }
 
-  const uint4 ww = reinterpret_cast<const uint4*>(kind == 0 ? p.q_w : p.k_w)[c];
-  float y[8];
-  y[0] = x[0] * inv_rms * bf16_lo(ww.x); y[1] = x[1] * inv_rms * bf16_hi(ww.x);
-  y[2] = x[2] * inv_rms * bf16_lo(ww.y); y[3] = x[3] * inv_rms * bf16_hi(ww.y);
-  y[4] = x[4] * inv_rms * bf16_lo(ww.z); y[5] = x[5] * inv_rms * bf16_hi(ww.z);
-  y[6] = x[6] * inv_rms * bf16_lo(ww.w); y[7] = x[7] * inv_rms * bf16_hi(ww.w);
-
-  // the partner dims (d + 64 for lanes 0-7, d - 64 for lanes 8-15)
-  float z[8];
+    float x[8];
+    x[0] = bf16_lo(w.xw.x); x[1] = bf16_hi(w.xw.x);
+    x[2] = bf16_lo(w.xw.y); x[3] = bf16_hi(w.xw.y);
+    x[4] = bf16_lo(w.xw.z); x[5] = bf16_hi(w.xw.z);
+    x[6] = bf16_lo(w.xw.w); x[7] = bf16_hi(w.xw.w);
+    float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) z[j] = dpp<kDppRowRor8>(y[j]);
+    for (int j = 0; j < 8; ++j) ss = fmaf(x[j], x[j], ss);
+    ss = row_sum16(ss);
+    const float inv_rms = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
 
-  int pos = live ? p.positions[t] : 0;
-  pos = pos < 0 ? 0 : (pos >= p.max_pos ? p.max_pos - 1 : pos);
-  const int d0 = 8 * (c & 7);  // angle index of this lane's first dim
-  const float4* cs = reinterpret_cast<const float4*>(p.cos_sin + static_cast<size_t>(pos) * kHeadDim + d0);
-  const float4 c0 = cs[0], c1 = cs[1];
-  const float4 s0 = cs[16], s1 = cs[17];  // the sines sit 64 floats further
-  const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-  // first half: y c - z s; second half: y c + z s
-  const float sgn = c < 8 ? -1.0f : 1.0f;
-  float o[8];
+    const uint4 ww = w.ww;
+    float y[8];
+    y[0] = x[0] * inv_rms * bf16_lo(ww.x); y[1] = x[1] * inv_rms * bf16_hi(ww.x);
+    y[2] = x[2] * inv_rms * bf16_lo(ww.y); y[3] = x[3] * inv_rms * bf16_hi(ww.y);
+    y[4] = x[4] * inv_rms * bf16_lo(ww.z); y[5] = x[5] * inv_rms * bf16_hi(ww.z);
+    y[6] = x[6] * inv_rms * bf16_lo(ww.w); y[7] = x[7] * inv_rms * bf16_hi(ww.w);
+
+    // the partner dims (d + 64 for lanes 0-7, d - 64 for lanes 8-15)
+    float z[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = fmaf(sgn * z[j], sv[j], y[j] * cv[j]);
-  const uint4 ow = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                              pack_bf16x2(o[6], o[7]));
-  if (!live) return;
-  if (kind == 0)
-    store_nt(reinterpret_cast<uint4*>(p.q_out + (static_cast<size_t>(t) * p.Hq + head) * kHeadDim) + c, ow);
-  else if (slot_ok)
-    store_nt(reinterpret_cast<uint4*>(p.k_cache + cache_off) + c, ow);
+    for (int j = 0; j < 8; ++j) z[j] = dpp<kDppRowRor8>(y[j]);
+
+    const float4 c0 = w.c0, c1 = w.c1, s0 = w.s0, s1 = w.s1;
+    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    // first half: y c - z s; second half: y c + z s
+    const float sgn = c < 8 ? -1.0f : 1.0f;
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = fmaf(sgn * z[j], sv[j], y[j] * cv[j]);
+    const uint4 ow = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                pack_bf16x2(o[6], o[7]));
+    if (!w.live) continue;
+    if (w.kind == 0)
+      store_nt(reinterpret_cast<uint4*>(p.q_out + (static_cast<size_t>(w.t) * p.Hq + w.head) * kHeadDim) + c, ow);
+    else if (slot_ok)
+      store_nt(reinterpret_cast<uint4*>(p.k_cache + cache_off) + c, ow);
+  }
 }
+
+// Rows per 16-lane group: kDeepRows once the launch has at least kDeepMinWgs
+// such workgroups (two per CU), else 1 (small launches are latency-bound and
+// want every row on its own lane group).
+constexpr int kDeepRows = 2;
+constexpr int64_t kDeepMinWgs = 512;
 
 }  // namespace
 
@@ -158,9 +225,13 @@ hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream) {
   p.eps = a.eps;
   const int64_t rows = static_cast<int64_t>(a.T) * (a.Hq + 2 * a.Hkv);
   if (rows == 0) return hipSuccess;
-  const unsigned grid = static_cast<unsigned>((rows + kRowsPerWg - 1) / kRowsPerWg);
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&qk_norm_rope_kernel), dim3(grid), dim3(kThreads), args, 0,
+  const int64_t deep_wgs = (rows + kRowGroups * kDeepRows - 1) / (kRowGroups * kDeepRows);
+  if (deep_wgs >= kDeepMinWgs)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&qk_norm_rope_kernel<kDeepRows>),
+                           dim3(static_cast<unsigned>(deep_wgs)), dim3(kThreads), args, 0, stream);
+  const unsigned grid = static_cast<unsigned>((rows + kRowGroups - 1) / kRowGroups);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&qk_norm_rope_kernel<1>), dim3(grid), dim3(kThreads), args, 0,
                          stream);
 }
 

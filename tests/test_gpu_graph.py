@@ -3,7 +3,7 @@ step): every replay, with other GPU work run eagerly in between, must give
 exactly the results of the same calls launched eagerly (the kernels reduce in
 a fixed order, so the outputs are bit-identical).  Covers KV append + split-K
 decode (pass 1 + merge), the mixed launch (in-kernel merge through the
-workspace counters) and the fused norm/rotary/append step."""
+workspace counters), the fused norm/rotary/append step and the sampler."""
 import pytest
 import torch
 
@@ -103,3 +103,20 @@ def test_graph_norm_rope(dev):
         fe.fe_qk_norm_rope_append(q_out, q, k, v, qw, kw, cs, pos, sm, kc, vc, c.eps)
 
     replay_matches(step, [q_out], dev, updated=[kc, vc])
+
+
+def test_graph_sampler(dev):
+    """The sampler step (two passes through a caller-owned workspace) as a
+    replayed graph, the way the vocabulary benchmark launches it."""
+    c = inputs.sampler_case(64, inputs.QWEN3_VOCAB, seed=11)
+    x, it = c.logits.to(dev), c.inv_temperature.to(dev)
+    B, V = c.logits.shape
+    probs = torch.empty(B, V, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, dtype=torch.float32, device=dev)
+    am = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(fe.fe_sampler_workspace_size(B, V), 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        fe.fe_sampler_softmax_argmax(probs, lse, am, x, it, workspace=ws)
+
+    replay_matches(step, [probs, lse, am], dev)
