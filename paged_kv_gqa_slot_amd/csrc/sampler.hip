@@ -9,8 +9,8 @@
 // fills the GPU.  Pass 1, one workgroup per (row, range): online max / sum of
 // 2^(s x log2 e - m) and the first maximal logit, as a partial in the
 // workspace.  Pass 2, one workgroup per (row, range): merge the row's
-// partials (a few dozen bytes), then write the range's probabilities; range 0
-// also writes the argmax and the LSE.  Each thread reads 8 bf16 logits per
+// partials (a few dozen bytes, one load per lane), then write the range's
+// probabilities; range 0 also writes the argmax and the LSE.  Each thread reads 8 bf16 logits per
 // 16-byte load.
 #include <math.h>
 
@@ -125,14 +125,21 @@ __global__ __launch_bounds__(kThreads) void sampler_write_kernel(SamplerParams p
   const int c = blockIdx.x % p.chunks;
   const int b = blockIdx.x / p.chunks;
   const float sc = row_scale(p, b);
-  // every thread merges the row's partials (a few dozen, read through the cache)
+  // every wave merges the row's partials (a few dozen): lane k loads
+  // partials k, k + 64, ... (one round trip for up to 64 ranges, where a
+  // serial walk took one per range), then a butterfly over the wave
   const Partial* pr = p.part + static_cast<size_t>(b) * p.chunks;
   float M = -INFINITY, Z = 0.f, best_v = -INFINITY;
   int best_i = 0x7fffffff;
-  for (int k = 0; k < p.chunks; ++k) {
+  for (int k = threadIdx.x & 63; k < p.chunks; k += 64) {
     const Partial q = pr[k];
     merge_ms(M, Z, q.m, q.sum);
     merge_best(best_v, best_i, q.best_v, q.best_i);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    merge_ms(M, Z, __shfl_xor(M, off), __shfl_xor(Z, off));
+    merge_best(best_v, best_i, __shfl_xor(best_v, off), __shfl_xor(best_i, off));
   }
   const bool empty = M == -INFINITY;
   if (c == 0 && threadIdx.x == 0) {
