@@ -148,6 +148,38 @@ int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cach
                         hipStream_t stream);
 
 /*
+ * fe_paged_kv_append of one new token per sequence fused into
+ * fe_paged_gqa_decode: one launch instead of two for the per-token step
+ * (append the token's K/V, then attend over the context that ends with it).
+ *   k_new, v_new  bf16 [B][Hkv][D]: sequence b's new K and V rows
+ *   slot_mapping  int32 [B]: the cache slot (block * BS + offset) of b's new
+ *                 token, which is position context_lens[b] - 1, the last of
+ *                 its context; a slot < 0 or >= num_blocks * BS is skipped
+ *                 (nothing written) and that position is read from the cache
+ *   k_cache, v_cache  written at those slots (bit copies), read as in
+ *                 fe_paged_gqa_decode
+ *   every other argument as fe_paged_gqa_decode (same workspace size)
+ * The result equals fe_paged_kv_append(k_new, v_new, slot_mapping, ..., T = B)
+ * followed by fe_paged_gqa_decode on the same arguments: the workgroup that
+ * holds b's last block writes the row and attends to it from registers.
+ * Preconditions (not checked): slot_mapping[b], when in range, is the slot of
+ * position context_lens[b] - 1 in b's block table (a slot anywhere else in a
+ * sequence's visible context makes that sequence's result unspecified);
+ * slots are distinct; with context_lens[b] = 0 nothing is written for b.
+ * Errors as fe_paged_gqa_decode, plus FE_ERR_NULL for NULL k_new, v_new or
+ * slot_mapping and FE_ERR_INVALID_ARG for k_new or v_new not 16-byte aligned.
+ * Source: ForgeEngine README, "What it implements" (paged KV cache written by
+ * the engine, CUDA paged GQA kernel); "Make the Engine Talk" section 1.2 (each
+ * generated token extends the cache, then one attention pass per token).
+ */
+int fe_paged_gqa_decode_append(void* out, float* lse, const void* q, const void* k_new, const void* v_new,
+                               const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                               int B, int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len,
+                               float scale, int num_partitions, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * Paged GQA prefill of a causal query chunk against the cached prefix.
  *   q              bf16 [total_q][Hq][D], sequences packed back to back
  *   query_start_loc  int32 [B + 1] DEVICE array; sequence b owns packed rows

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     fe_kv_allocator_seq_len,
     fe_last_error,
     fe_paged_gqa_decode,
+    fe_paged_gqa_decode_append,
     fe_paged_gqa_decode_num_partitions,
     fe_paged_gqa_decode_workspace_size,
     fe_paged_gqa_mixed,

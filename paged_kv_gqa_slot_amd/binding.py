@@ -49,6 +49,8 @@ def load_library():
     lib.fe_paged_gqa_decode_num_partitions.restype = I
     lib.fe_paged_gqa_decode.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fe_paged_gqa_decode.restype = I
+    lib.fe_paged_gqa_decode_append.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, Z, P]
+    lib.fe_paged_gqa_decode_append.restype = I
     lib.fe_paged_gqa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, P]
     lib.fe_paged_gqa_prefill_chunk.restype = I
     lib.fe_paged_gqa_prefill_chunk_ex.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, I, P]
@@ -167,6 +169,31 @@ def fe_paged_gqa_decode(out, lse, q, k_cache, v_cache, block_tables, context_len
         _dev(context_lens, torch.int32, "context_lens", 1), B, Hq, Hkv, D, BS, NB, int(max_context_len),
         float(scale), int(num_partitions), ws_ptr, ws_have, _stream(stream))
     _check(rc, "fe_paged_gqa_decode")
+
+
+def fe_paged_gqa_decode_append(out, lse, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                               max_context_len: int, scale: float, num_partitions: int = 0, workspace=None,
+                               stream=None) -> None:
+    """Append of one new K/V row per sequence (into slot_mapping[b], the
+    slot of position context_lens[b] - 1) fused into decode attention.
+    Same workspace as fe_paged_gqa_decode; one is allocated when not given."""
+    B, Hq, D = q.shape
+    NB, Hkv, BS, _ = k_cache.shape
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D) or tuple(slot_mapping.shape) != (B,):
+        raise ValueError("k_new/v_new must be [B][Hkv][D] and slot_mapping [B]")
+    ws_bytes = fe_paged_gqa_decode_workspace_size(B, Hq, Hkv, D, max_context_len, num_partitions)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, torch.uint8, "workspace") if workspace is not None else None
+    ws_have = workspace.numel() if workspace is not None else 0
+    rc = load_library().fe_paged_gqa_decode_append(
+        _dev(out, torch.bfloat16, "out", 3), _dev(lse, torch.float32, "lse", 2), _dev(q, torch.bfloat16, "q", 3),
+        _dev(k_new, torch.bfloat16, "k_new", 3), _dev(v_new, torch.bfloat16, "v_new", 3),
+        _dev(slot_mapping, torch.int32, "slot_mapping", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
+        _dev(v_cache, torch.bfloat16, "v_cache", 4), _dev(block_tables, torch.int32, "block_tables", 2),
+        block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens", 1), B, Hq, Hkv, D, BS, NB,
+        int(max_context_len), float(scale), int(num_partitions), ws_ptr, ws_have, _stream(stream))
+    _check(rc, "fe_paged_gqa_decode_append")
 
 
 def fe_paged_gqa_prefill_chunk(out, lse, q, query_start_loc, k_cache, v_cache, block_tables, context_lens,

@@ -151,6 +151,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   DecodeParams prm = make_decode_params(a.q, a.k_cache, a.v_cache, a.block_tables, a.max_blocks_per_seq,
                                         a.context_lens, a.out, a.lse, a.B, a.Hq, a.Hkv, a.num_blocks,
                                         a.max_context_len, a.scale, a.plan.partitions, a.plan.part_blocks);
+  if (a.k_new) {
+    prm.k_new = static_cast<const uint16_t*>(a.k_new);
+    prm.v_new = static_cast<const uint16_t*>(a.v_new);
+    prm.new_slots = a.new_slots;
+    prm.k_cache_w = static_cast<uint16_t*>(const_cast<void*>(a.k_cache));
+    prm.v_cache_w = static_cast<uint16_t*>(const_cast<void*>(a.v_cache));
+    prm.num_slots = static_cast<int64_t>(a.num_blocks) * kBlockSize;
+  }
   if (prm.P > 1) {
     prm.o_part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + a.plan.o_part_offset);
     prm.lse_part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + a.plan.lse_part_offset);

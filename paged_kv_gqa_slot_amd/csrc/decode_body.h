@@ -60,6 +60,15 @@ struct DecodeParams {
   int* arrivals;          // fused merge: [B][Hkv] partitions finished so far (zero between calls)
   const int32_t* q_rows;  // row of sequence b in q / out / lse (nullptr: row b)
   int q_rows_count;       // rows of q / out / lse when q_rows is used (rows are clamped into it)
+  // Fused append (nullptr k_new: none): sequence b's new K/V rows
+  // k_new/v_new [B][Hkv][D] go to cache slot new_slots[b], the slot of its
+  // position L_b - 1, written by the workgroup that holds that block.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* new_slots;
+  uint16_t* k_cache_w;  // the pools again, writable (fused append only)
+  uint16_t* v_cache_w;
+  int64_t num_slots;
   int max_blocks, B, Hq, Hkv, num_blocks, ctx_cap;
   int P, part_blocks;
   float scale_log2;  // |scale| * log2(e)
@@ -265,7 +274,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<
   const int nb = max(0, blk1 - blk0);
   // tokens in the sequence's last block; that block is masked if partial
   const int rem = L - (nblk - 1) * kBlockSize;
-  const bool has_tail = nb > 0 && blk1 == nblk && rem < kBlockSize;
+  // With a fused append the sequence's last block always takes the tail path
+  // below (full or not), which writes the new row and patches it in.
+  const bool fuse = p.k_new != nullptr && nb > 0 && blk1 == nblk;
+  const bool has_tail = nb > 0 && blk1 == nblk && (rem < kBlockSize || fuse);
   const int nfull = nb - (has_tail ? 1 : 0);
 
   State<G> st;
@@ -304,9 +316,37 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<
     }
   }
   if (has_tail && wave == (nb - 1) % W) {
-    const size_t o = static_cast<size_t>(__builtin_amdgcn_readlane(ids, (nb - 1) / W)) * blk_stride;
+    const int id = __builtin_amdgcn_readlane(ids, (nb - 1) / W);
+    const size_t o = static_cast<size_t>(id) * blk_stride;
     const int bytes = rem * kHeadDim * 2;
     load_tile(ring[0], tile_rsrc(kg + o, bytes), tile_rsrc(vg + o, bytes), lane);
+    if (fuse) {
+      // The new token: row rem - 1 of this block.  Write it into its slot (as
+      // fe_paged_kv_append does: skipped unless 0 <= slot < num_slots) and,
+      // when the slot is that row's, take its K/V from registers: the tile
+      // load above may or may not have seen the store.
+      const int64_t slot = p.new_slots[b];
+      const size_t nrow = (static_cast<size_t>(b) * p.Hkv + g) * kHeadDim;
+      const uint4 kn = reinterpret_cast<const uint4*>(p.k_new + nrow)[c];
+      const uint4 vn = reinterpret_cast<const uint4*>(p.v_new + nrow)[c];
+      if (slot >= 0 && slot < p.num_slots) {
+        if (r == 0) {
+          const size_t dst = ((static_cast<size_t>(slot / kBlockSize) * p.Hkv + g) * kBlockSize + slot % kBlockSize) *
+                             kHeadDim;
+          reinterpret_cast<uint4*>(p.k_cache_w + dst)[c] = kn;
+          reinterpret_cast<uint4*>(p.v_cache_w + dst)[c] = vn;
+        }
+        const int row = rem - 1;
+        if (slot == static_cast<int64_t>(id) * kBlockSize + row && r == (row & 3)) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (j == (row >> 2)) {
+              ring[0].k[j] = kn;
+              ring[0].v[j] = vn;
+            }
+        }
+      }
+    }
     consume<G, true>(st, ring[0], qw, p.scale_log2, r, rem);
   }
 

@@ -102,11 +102,13 @@ int fe_paged_gqa_decode_num_partitions(int B, int Hq, int Hkv, int D, int max_co
   return plan.partitions;
 }
 
-int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
-                        const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens, int B,
-                        int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale,
-                        int num_partitions, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  static const char* fn = "fe_paged_gqa_decode";
+namespace {
+
+int decode_call(const char* fn, void* out, float* lse, const void* q, const void* k_new, const void* v_new,
+                const int32_t* slot_mapping, bool fused, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens, int B, int Hq,
+                int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale, int num_partitions,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   try {
     if (B < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_partitions < 0)
       return fail(FE_ERR_INVALID_ARG, fn,
@@ -115,8 +117,12 @@ int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cach
     if (!isfinite(scale)) return fail(FE_ERR_INVALID_ARG, fn, "scale must be finite");
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
       return fail(FE_ERR_NULL, fn, "out, q, k_cache, v_cache, block_tables, context_lens must not be NULL");
+    if (fused && (!k_new || !v_new || !slot_mapping))
+      return fail(FE_ERR_NULL, fn, "k_new, v_new, slot_mapping must not be NULL");
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
       return fail(FE_ERR_INVALID_ARG, fn, "out, q, k_cache, v_cache, workspace must be 16-byte aligned");
+    if (fused && (!aligned16(k_new) || !aligned16(v_new)))
+      return fail(FE_ERR_INVALID_ARG, fn, "k_new, v_new must be 16-byte aligned");
     fe::DecodePlan plan;
     if (!fe::plan_decode(B, Hq, Hkv, max_context_len, num_partitions, &plan))
       return fail(FE_ERR_INVALID_ARG, fn, "cannot plan these sizes");
@@ -128,11 +134,38 @@ int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cach
       return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     fe::DecodeArgs a{out, lse, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv,
                      num_blocks, max_context_len, scale, plan, workspace};
+    if (fused) {
+      a.k_new = k_new;
+      a.v_new = v_new;
+      a.new_slots = slot_mapping;
+    }
     const hipError_t e = fe::launch_decode(a, stream);
     return e == hipSuccess ? FE_OK : hip_fail(e, fn);
   } catch (...) {
     return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
   }
+}
+
+}  // namespace
+
+int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens, int B,
+                        int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale,
+                        int num_partitions, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_call("fe_paged_gqa_decode", out, lse, q, nullptr, nullptr, nullptr, false, k_cache, v_cache,
+                     block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, num_blocks, max_context_len,
+                     scale, num_partitions, workspace, workspace_bytes, stream);
+}
+
+int fe_paged_gqa_decode_append(void* out, float* lse, const void* q, const void* k_new, const void* v_new,
+                               const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                               int B, int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len,
+                               float scale, int num_partitions, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return decode_call("fe_paged_gqa_decode_append", out, lse, q, k_new, v_new, slot_mapping, true, k_cache, v_cache,
+                     block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, num_blocks, max_context_len,
+                     scale, num_partitions, workspace, workspace_bytes, stream);
 }
 
 namespace {

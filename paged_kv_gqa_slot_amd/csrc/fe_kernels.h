@@ -42,6 +42,10 @@ struct DecodeArgs {
   float scale;
   DecodePlan plan;
   void* workspace;
+  // fused append (fe_paged_gqa_decode_append): nullptr k_new means none
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* new_slots = nullptr;
 };
 
 struct PrefillArgs {

@@ -91,6 +91,35 @@ def test_decode_batch_zero_is_noop(lib):
     assert dec(lib, B=0) == OK
 
 
+def dec_append(lib, **kw):
+    a = dict(out=P, lse=None, q=P, kn=P, vn=P, sm=P, k=P, v=P, bt=P, mb=8, cl=P, B=2, Hq=32, Hkv=8, D=128, BS=16,
+             NB=64, mcl=128, scale=0.088, parts=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.fe_paged_gqa_decode_append(a["out"], a["lse"], a["q"], a["kn"], a["vn"], a["sm"], a["k"], a["v"],
+                                          a["bt"], a["mb"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["BS"],
+                                          a["NB"], a["mcl"], a["scale"], a["parts"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_append_argument_errors(lib):
+    # the fused call checks everything the decode call does ...
+    assert dec_append(lib, q=None) == NULL
+    assert dec_append(lib, bt=None) == NULL
+    assert dec_append(lib, Hq=30) == INVALID
+    assert dec_append(lib, scale=float("nan")) == INVALID
+    assert dec_append(lib, D=64) == UNSUPPORTED
+    assert dec_append(lib, BS=32) == UNSUPPORTED
+    need = lib.fe_paged_gqa_decode_workspace_size(2, 32, 8, 128, 4096, 8)
+    assert dec_append(lib, mcl=4096, mb=256, parts=8, ws=P, wsb=need - 1) == WORKSPACE
+    # ... and the new rows and their slots
+    for name in ("kn", "vn", "sm"):
+        assert dec_append(lib, **{name: None}) == NULL
+        assert "slot_mapping" in fe.fe_last_error()
+    assert dec_append(lib, kn=P + 4) == INVALID
+    assert dec_append(lib, vn=P + 8) == INVALID
+    assert "16-byte" in fe.fe_last_error()
+    assert dec_append(lib, B=0) == OK
+
+
 def test_workspace_and_partition_queries(lib):
     ws = lib.fe_paged_gqa_decode_workspace_size
     npart = lib.fe_paged_gqa_decode_num_partitions

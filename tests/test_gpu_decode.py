@@ -185,3 +185,95 @@ def test_decode_negative_scale(dev):
     w = inputs.custom("decode", 3, 16, 4, [300, 47, 1000], 78, append=1)
     w.scale = -w.scale
     run_decode(w, dev, parts=(1, 4, 0), label="negative scale")
+
+
+# -- append fused into decode (fe_paged_gqa_decode_append) ------------------------
+
+def per_sequence_rows(w, layer=0):
+    """The workload's new rows as the fused call takes them: one per sequence
+    ([B][Hkv][D], slot -1 and zero rows where a sequence is empty)."""
+    lay = w.layers[layer]
+    lens = w.context_lens.tolist()
+    kn = torch.zeros(w.B, w.Hkv, 128, dtype=torch.bfloat16)
+    vn = torch.zeros_like(kn)
+    slots = torch.full((w.B,), -1, dtype=torch.int32)
+    i = 0
+    for b, L in enumerate(lens):
+        if L > 0:
+            kn[b], vn[b], slots[b] = lay.k_new[i], lay.v_new[i], w.slot_mapping[i]
+            i += 1
+    assert i == w.slot_mapping.numel()
+    return kn, vn, slots
+
+
+def run_decode_append(w, dev, parts=(0,), label="", layer=0, slots_override=None, pre=None):
+    """Fused append + decode against the oracle's append followed by its
+    decode: the pools bit for bit after every call, attention to the gate.
+    `pre` (host pools) replaces the workload's pools as the starting state."""
+    lay = w.layers[layer]
+    kn, vn, slots = per_sequence_rows(w, layer)
+    if slots_override is not None:
+        slots = slots_override
+    k0, v0 = (lay.k_cache, lay.v_cache) if pre is None else pre
+    # the oracle skips negative slots; slots past the pool are skipped too
+    ref_slots = slots.clone()
+    ref_slots[ref_slots >= w.num_blocks * 16] = -1
+    rk, rv = oracle.append(kn, vn, ref_slots, k0, v0)  # uint16 images of the pools
+    ro, rl = oracle.decode(lay.q, rk, rv, w.block_tables, w.context_lens, w.scale)
+    q, bt, lens = lay.q.to(dev), w.block_tables.to(dev), w.context_lens.to(dev)
+    kn_d, vn_d, sl_d = kn.to(dev), vn.to(dev), slots.to(dev)
+    for P in parts:
+        kc, vc = k0.to(dev), v0.to(dev)
+        out = torch.full((w.B, w.Hq, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+        lse = torch.full((w.B, w.Hq), float("nan"), dtype=torch.float32, device=dev)
+        fe.fe_paged_gqa_decode_append(out, lse, q, kn_d, vn_d, sl_d, kc, vc, bt, lens, w.max_context_len, w.scale,
+                                      num_partitions=P)
+        torch.cuda.synchronize()
+        assert np.array_equal(u16(kc), rk), (label, P, "K pool differs after the fused append")
+        assert np.array_equal(u16(vc), rv), (label, P, "V pool differs after the fused append")
+        assert_attention(out, lse, ro, rl, f"{label} fused P={P}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_append_small(dev, G):
+    # full last blocks (16, 32, 256) and partial ones, a single token, an empty sequence
+    lens = [1, 15, 16, 17, 100, 256, 0, 33, 32]
+    w = inputs.custom("decode", len(lens), 2 * G, 2, lens, 300 + G, append=1, poison="nan")
+    run_decode_append(w, dev, parts=(1, 2, 3, 0), label=f"fused small G={G}")
+
+
+def test_decode_append_padding_and_out_of_range_slots(dev):
+    """A padding slot (-1) and a slot past the pool write nothing; those
+    sequences read their last position from the cache as it is (here: their
+    rows, already written by an earlier step)."""
+    lens = [40, 16, 77, 5]
+    w = inputs.custom("decode", 4, 8, 2, lens, 311, append=1, poison="nan")
+    kn, vn, slots = per_sequence_rows(w)
+    earlier = torch.full_like(slots, -1)
+    earlier[1], earlier[2] = slots[1], slots[2]
+    k0, v0 = oracle.append(kn, vn, earlier, w.layers[0].k_cache, w.layers[0].v_cache)
+    pre = tuple(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) for x in (k0, v0))
+    slots[1] = -1
+    slots[2] = w.num_blocks * 16 + 5
+    run_decode_append(w, dev, parts=(1, 0), label="fused padding", slots_override=slots, pre=pre)
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_decode_append_qwen3_4b_b64(dev, seed):
+    """The serving-concurrency workload, its append fused into the decode call."""
+    w = inputs.make("qwen3_4b_b64_ctx1024-8192", seed=seed, poison="nan")
+    run_decode_append(w, dev, parts=(0, 1, 16), label=f"fused 4b b64 seed {seed}")
+
+
+def test_decode_append_qwen3_4b_b4_small_batch(dev):
+    """Four sequences of the Qwen3-4B layer shape with contexts as in the
+    36-layer workload (256..2048 tokens), each with a new token."""
+    g = torch.Generator().manual_seed(321)
+    lens = torch.randint(256, 2049, (4,), generator=g).tolist()
+    w = inputs.custom("decode", 4, 32, 8, lens, 321, append=1, poison="nan")
+    run_decode_append(w, dev, parts=(0, 1, 8), label="fused 4b b4")
+
+
+def test_decode_append_qwen3_0_6b_b1_ctx128(dev):
+    w = inputs.make("qwen3_0.6b_b1_ctx128", poison="nan")
+    run_decode_append(w, dev, parts=(0, 1, 8), label="fused 0.6b b1")

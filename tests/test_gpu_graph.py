@@ -3,7 +3,8 @@ step): every replay, with other GPU work run eagerly in between, must give
 exactly the results of the same calls launched eagerly (the kernels reduce in
 a fixed order, so the outputs are bit-identical).  Covers KV append + split-K
 decode (pass 1 + merge), the mixed launch (in-kernel merge through the
-workspace counters), the fused norm/rotary/append step and the sampler."""
+workspace counters), append fused into decode, the fused norm/rotary/append step
+and the sampler."""
 import pytest
 import torch
 
@@ -103,6 +104,28 @@ def test_graph_norm_rope(dev):
         fe.fe_qk_norm_rope_append(q_out, q, k, v, qw, kw, cs, pos, sm, kc, vc, c.eps)
 
     replay_matches(step, [q_out], dev, updated=[kc, vc])
+
+
+def test_graph_decode_append(dev):
+    """Append fused into split-K decode (pass 1 writes the new rows, pass 2
+    merges) as a replayed graph."""
+    lens = [700, 1500, 64, 999, 16, 1]
+    w = inputs.custom("decode", 6, 32, 8, lens, 81, append=1)
+    lay = w.layers[0]
+    kn, vn = lay.k_new.to(dev), lay.v_new.to(dev)  # every sequence has one new token
+    slots = w.slot_mapping.to(dev)
+    kc, vc = lay.k_cache.to(dev), lay.v_cache.to(dev)
+    q, bt, cl = lay.q.to(dev), w.block_tables.to(dev), w.context_lens.to(dev)
+    out = torch.empty(6, 32, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(6, 32, dtype=torch.float32, device=dev)
+    ws = torch.empty(fe.fe_paged_gqa_decode_workspace_size(6, 32, 8, 128, w.max_context_len, 4), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fe.fe_paged_gqa_decode_append(out, lse, q, kn, vn, slots, kc, vc, bt, cl, w.max_context_len, w.scale,
+                                      num_partitions=4, workspace=ws)
+
+    replay_matches(step, [out, lse], dev, updated=[kc, vc])
 
 
 def test_graph_sampler(dev):
