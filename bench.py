@@ -499,6 +499,15 @@ def main():
                 fe.fe_paged_kv_append(x["kn"], x["vn"], slots, x["kc"], x["vc"])
             attend(x)
 
+    # one new token per sequence (slot rows in sequence order): the same step
+    # with each layer's append fused into its decode call
+    fused_ok = is_decode and do_append and slots.numel() == w.B
+
+    def step_fused():
+        for x in L:
+            fe.fe_paged_gqa_decode_append(out, lse, x["q"], x["kn"], x["vn"], slots, x["kc"], x["vc"], bt, lens, mcl,
+                                          w.scale, num_partitions=args.partitions, workspace=ws)
+
     log(f"warmup {args.warmup} steps (partitions={P}, workspace={ws_bytes} B)")
     for _ in range(args.warmup):
         step()
@@ -537,6 +546,26 @@ def main():
             ms_per_step, launch = graph_ms, "hip_graph"
     else:
         graph_ms = None
+    separate_ms = ms_per_step
+    append_mode = "separate" if do_append else "none"
+    fused_eager_ms = fused_graph_ms = None
+    if fused_ok:
+        # the step is timed both ways; `value` takes the faster (the same
+        # rows reach the same slots either way, so the caches stay as they were)
+        for _ in range(args.warmup):
+            step_fused()
+        fused_eager_ms = time_steps(step_fused)
+        if fused_eager_ms < ms_per_step:
+            ms_per_step, launch, append_mode = fused_eager_ms, "eager", "fused"
+        if not args.eager:
+            graph_f = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph_f):
+                step_fused()
+            for _ in range(args.warmup):
+                graph_f.replay()
+            fused_graph_ms = time_steps(graph_f.replay)
+            if fused_graph_ms < ms_per_step:
+                ms_per_step, launch, append_mode = fused_graph_ms, "hip_graph", "fused"
 
     # per-kernel timing of the attention call (the dominant kernel), same stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -640,8 +669,11 @@ def main():
     cfg = {"workload": spec.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": 128,
            "block_size": 16, "layers": nl, "kv_tokens": w.kv_tokens, "max_context_len": mcl,
            "append_tokens_per_step": int(slots.numel()) * nl, "num_partitions": P, "seed": w.seed,
-           "launch": launch, "eager_ms_per_step": round(eager_ms, 5),
-           "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None}
+           "launch": launch, "append": append_mode, "eager_ms_per_step": round(eager_ms, 5),
+           "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
+           "separate_append_ms_per_step": round(separate_ms, 5) if do_append else None,
+           "fused_eager_ms_per_step": None if fused_eager_ms is None else round(fused_eager_ms, 5),
+           "fused_graph_ms_per_step": None if fused_graph_ms is None else round(fused_graph_ms, 5)}
     rec = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": not is_mixed,
            "scaling": "weak",
