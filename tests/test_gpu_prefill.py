@@ -47,20 +47,20 @@ def run_prefill(w, dev, label, rows=None, lens_override=None, key_groups=None):
 # Tile shapes: None is fe_paged_gqa_prefill_chunk (automatic: two key groups
 # per workgroup for Hq/Hkv <= 4 on these small grids, one above); 1 forces one
 # key group through fe_paged_gqa_prefill_chunk_ex.  Forcing one group where
-# it is already the default repeats the automatic case and is skipped.
+# it is already the default would repeat the automatic case, so those
+# combinations are not generated.
 KEY_GROUPS = [None, 1]
 
 
-def _skip_repeat(G, kg):
-    if kg == 1 and G > 4:
-        pytest.skip("one key group is already the automatic tile for Hq/Hkv > 4")
+def tile_cases(Gs):
+    """(G, key_groups) pairs: both tiles where two key groups are the
+    default (Hq/Hkv <= 4), the automatic tile alone above."""
+    return [(G, kg) for G in Gs for kg in KEY_GROUPS if not (kg == 1 and G > 4)]
 
 
-@pytest.mark.parametrize("kg", KEY_GROUPS)
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("G,kg", tile_cases([1, 2, 3, 4, 5, 6, 7, 8]))
 @pytest.mark.parametrize("poison", ["nan", "large"])
 def test_prefill_small(dev, G, poison, kg):
-    _skip_repeat(G, kg)
     chunks = [1, 31, 33, 100]
     prefix = [0, 17, 130, 64]
     lens = [p + c for p, c in zip(prefix, chunks)]
@@ -94,8 +94,7 @@ def _ragged(spec, lens, chunks, seed, poison):
                            layers=[lay])
 
 
-@pytest.mark.parametrize("kg", KEY_GROUPS)
-@pytest.mark.parametrize("G", [1, 3, 4, 6, 8])
+@pytest.mark.parametrize("G,kg", tile_cases([1, 3, 4, 6, 8]))
 def test_prefill_tile_counts(dev, G, kg):
     """Key ranges of 1 to 18 64-key tiles (odd and even counts, so the two
     wave groups that split the keys get equal or unequal shares, or one gets
@@ -103,17 +102,14 @@ def test_prefill_tile_counts(dev, G, kg):
     lens = [64, 65, 128, 190, 257, 1000, 1088, 700]
     chunks = [64, 1, 100, 190, 3, 300, 1, 129]
     spec = inputs.Spec("prefill_ragged", "prefill", len(lens), 2 * G, 2, min(lens), max(lens), append=0, chunk=0)
-    _skip_repeat(G, kg)
     w = _ragged(spec, lens, chunks, 400 + G, "nan")
     run_prefill(w, dev, f"tile counts G={G} key_groups={kg}", key_groups=kg)
 
 
-@pytest.mark.parametrize("kg", KEY_GROUPS)
-@pytest.mark.parametrize("G,lens", [(4, [9000, 8300]), (8, [4500, 4200])])
+@pytest.mark.parametrize("G,lens,kg", [(4, [9000, 8300], None), (4, [9000, 8300], 1), (8, [4500, 4200], None)])
 def test_prefill_long_key_range(dev, G, lens, kg):
     """More than 64 tiles of keys per wave group, so the kernel's per-wave
     list of staged block ids is reloaded mid-sequence."""
-    _skip_repeat(G, kg)
     w = inputs.custom("prefill", 2, 2 * G, 2, lens, 500 + G, append=64, chunk=64, poison="nan")
     run_prefill(w, dev, f"long key range G={G} key_groups={kg}", key_groups=kg)
 
