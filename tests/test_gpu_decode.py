@@ -234,7 +234,7 @@ def run_decode_append(w, dev, parts=(0,), label="", layer=0, slots_override=None
         assert_attention(out, lse, ro, rl, f"{label} fused P={P}")
 
 
-@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_decode_append_small(dev, G):
     # full last blocks (16, 32, 256) and partial ones, a single token, an empty sequence
     lens = [1, 15, 16, 17, 100, 256, 0, 33, 32]
