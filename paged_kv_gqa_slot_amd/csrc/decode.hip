@@ -8,7 +8,9 @@
 // decode_body.h.  With one partition the kernel writes the bf16 output and the
 // LSE; otherwise every partition writes a normalised fp32 partial and its LSE,
 // and pass 2 (gqa_decode_merge_kernel) combines the partitions of a row by
-// log-sum-exp.
+// log-sum-exp.  With a fused append (fe_paged_gqa_decode_append), pass 1 also
+// writes each sequence's new K/V row into its slot, from the workgroup that
+// holds the sequence's last block.
 #include <math.h>
 
 #include "decode_body.h"

@@ -20,7 +20,9 @@
 //   rare).  PV: v_dot2_f32_bf16 with the softmax weights of two tokens
 //   packed as a bf16 pair against the matching V words (fp32
 //   accumulation).  A partially filled last block is handled after the main
-//   loop by a masked variant of the same step.
+//   loop by a masked variant of the same step; with a fused append the last
+//   block always goes that way, and there the new token's row is written to
+//   the cache and patched into the loaded tile.
 //
 // At the end the 4 rows and W waves are merged (max-shifted sums) through
 // cross-lane shuffles and LDS.  An unsplit sequence gets its bf16 output and
