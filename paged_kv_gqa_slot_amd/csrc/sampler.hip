@@ -121,13 +121,16 @@ __global__ __launch_bounds__(kThreads) void sampler_partial_kernel(SamplerParams
   }
 }
 
-__global__ __launch_bounds__(kThreads) void sampler_write_kernel(SamplerParams p) {
-  const int c = blockIdx.x % p.chunks;
-  const int b = blockIdx.x / p.chunks;
-  const float sc = row_scale(p, b);
-  // every wave merges the row's partials (a few dozen): lane k loads
-  // partials k, k + 64, ... (one round trip for up to 64 ranges, where a
-  // serial walk took one per range), then a butterfly over the wave
+// Every wave merges the row's partials (a few dozen): lane k loads partials
+// k, k + 64, ... (one round trip for up to 64 ranges, where a serial walk took
+// one per range), then a butterfly over the wave.  Range 0 writes the argmax
+// and the LSE.
+struct RowTotals {
+  float M, Z;
+  bool empty;
+};
+
+__device__ __forceinline__ RowTotals merge_row(const SamplerParams& p, int b, int c) {
   const Partial* pr = p.part + static_cast<size_t>(b) * p.chunks;
   float M = -INFINITY, Z = 0.f, best_v = -INFINITY;
   int best_i = 0x7fffffff;
@@ -146,20 +149,36 @@ __global__ __launch_bounds__(kThreads) void sampler_write_kernel(SamplerParams p
     p.argmax[b] = empty ? 0 : best_i;
     if (p.lse) p.lse[b] = empty ? -INFINITY : (M + log2f(Z)) * kLn2;
   }
-  if (!p.probs) return;
-  const float invZ = empty ? 0.f : 1.0f / Z;
+  return RowTotals{M, Z, empty};
+}
+
+__global__ __launch_bounds__(kThreads) void sampler_write_kernel(SamplerParams p) {
+  const int c = blockIdx.x % p.chunks;
+  const int b = blockIdx.x / p.chunks;
+  if (!p.probs) {  // argmax and LSE only: the logits are not read again
+    merge_row(p, b, c);
+    return;
+  }
+  const float sc = row_scale(p, b);
   const int u0 = c * p.chunk_units;
   const int u1 = min(u0 + p.chunk_units, p.V / 8);
   const uint4* row = reinterpret_cast<const uint4*>(p.logits + static_cast<size_t>(b) * p.V);
-  float4* out = reinterpret_cast<float4*>(p.probs + static_cast<size_t>(b) * p.V);
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  // This thread's logits are loaded first, so their round trip overlaps the
+  // partial merge.  Every load is issued, at a unit clamped into the row (a
+  // load under a branch would make the compiler wait for it early); units
+  // past the range are not used.
   u32x4_t w[kUnitsPerThread];
+  const int last = max(u1 - 1, 0);
 #pragma unroll
   for (int k = 0; k < kUnitsPerThread; ++k) {
-    const int u = u0 + threadIdx.x + k * kThreads;
-    w[k] = u < u1 ? *reinterpret_cast<const u32x4_t*>(&row[u]) : u32x4_t{0, 0, 0, 0};
+    const int u = min(u0 + static_cast<int>(threadIdx.x) + k * kThreads, last);
+    w[k] = *reinterpret_cast<const u32x4_t*>(&row[u]);
   }
+  const RowTotals t = merge_row(p, b, c);
+  const float invZ = t.empty ? 0.f : 1.0f / t.Z;
+  float4* out = reinterpret_cast<float4*>(p.probs + static_cast<size_t>(b) * p.V);
 #pragma unroll
   for (int k = 0; k < kUnitsPerThread; ++k) {
     const int u = u0 + threadIdx.x + k * kThreads;
@@ -168,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void sampler_write_kernel(SamplerParams p
                         bf16_lo(w[k][2]), bf16_hi(w[k][2]), bf16_lo(w[k][3]), bf16_hi(w[k][3])};
     float e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = empty ? 0.f : fast_exp2(x[j] * sc - M) * invZ;
+    for (int j = 0; j < 8; ++j) e[j] = t.empty ? 0.f : fast_exp2(x[j] * sc - t.M) * invZ;
     const f32x4_t lo = {e[0], e[1], e[2], e[3]}, hi = {e[4], e[5], e[6], e[7]};
     *reinterpret_cast<f32x4_t*>(&out[2 * u]) = lo;
     *reinterpret_cast<f32x4_t*>(&out[2 * u + 1]) = hi;
