@@ -277,3 +277,23 @@ def test_decode_append_qwen3_4b_b4_small_batch(dev):
 def test_decode_append_qwen3_0_6b_b1_ctx128(dev):
     w = inputs.make("qwen3_0.6b_b1_ctx128", poison="nan")
     run_decode_append(w, dev, parts=(0, 1, 8), label="fused 0.6b b1")
+
+
+def test_decode_append_random_shapes(dev):
+    """Seeded random shapes for the fused call: group size, KV heads, batch,
+    ragged lengths (zeros and whole blocks included) and partition counts."""
+    g = torch.Generator().manual_seed(2024)
+    for case in range(12):
+        G = int(torch.randint(1, 9, (1,), generator=g))
+        Hkv = [1, 2, 8][int(torch.randint(0, 3, (1,), generator=g))]
+        B = int(torch.randint(1, 10, (1,), generator=g))
+        lens = torch.randint(0, 700, (B,), generator=g)
+        lens[torch.rand(B, generator=g) < 0.2] = 0
+        whole = torch.rand(B, generator=g) < 0.3
+        lens[whole] = (lens[whole] // 16 + 1) * 16
+        lens = lens.tolist()
+        if max(lens) == 0:
+            lens[0] = 1
+        parts = (0, 1, int(torch.randint(2, 10, (1,), generator=g)))
+        w = inputs.custom("decode", B, G * Hkv, Hkv, lens, 700 + case, append=1, poison="nan")
+        run_decode_append(w, dev, parts=parts, label=f"fused random #{case} G={G} Hkv={Hkv} lens={lens}")
