@@ -6,7 +6,8 @@ blocks, which later requests reuse.  Every step's K/V rows go through
 fe_paged_kv_append at the allocator's slots, and decode (and, for prompts,
 the chunked prefill) runs over the allocator's block tables; each result
 matches the fp64 oracle run on a host copy of the same pools, and no KV
-block is left allocated at the end.
+block is left allocated at the end.  The decode steps run either as append +
+decode or as the fused fe_paged_gqa_decode_append call.
 """
 import numpy as np
 import pytest
@@ -28,7 +29,8 @@ def dev():
     return torch.device("cuda:0")
 
 
-def test_allocator_driven_serving(dev):
+@pytest.mark.parametrize("fused", [False, True])
+def test_allocator_driven_serving(dev, fused):
     NB, Hq, Hkv, max_seqs, mbps = 160, 32, 8, 4, 48
     g = torch.Generator().manual_seed(900)
     alloc = fe.KVAllocator(NB, BS, max_seqs, mbps)
@@ -86,14 +88,25 @@ def test_allocator_driven_serving(dev):
             continue
         # one decode step for every running request
         seqs = [running[r]["seq"] for r in running]
-        for s in seqs:
-            append(s, 1)
+        if fused:
+            # one new row per sequence at the allocator's slot, appended by the decode call itself
+            slots = torch.from_numpy(np.concatenate([alloc.append(s, 1) for s in seqs]))
+            kn, vn = rows(len(seqs))
+            kc_h, vc_h = oracle.append(kn, vn, slots, kc_h, vc_h)
+        else:
+            for s in seqs:
+                append(s, 1)
         bt, cl = alloc.batch(seqs)
         q = torch.randn(len(seqs), Hq, D, generator=g).to(torch.bfloat16)
         out = torch.empty(len(seqs), Hq, D, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(len(seqs), Hq, dtype=torch.float32, device=dev)
-        fe.fe_paged_gqa_decode(out, lse, q.to(dev), kc, vc, torch.from_numpy(bt).to(dev),
-                               torch.from_numpy(cl).to(dev), int(cl.max()), scale)
+        if fused:
+            fe.fe_paged_gqa_decode_append(out, lse, q.to(dev), kn.to(dev), vn.to(dev), slots.to(dev), kc, vc,
+                                          torch.from_numpy(bt).to(dev), torch.from_numpy(cl).to(dev), int(cl.max()),
+                                          scale)
+        else:
+            fe.fe_paged_gqa_decode(out, lse, q.to(dev), kc, vc, torch.from_numpy(bt).to(dev),
+                                   torch.from_numpy(cl).to(dev), int(cl.max()), scale)
         torch.cuda.synchronize()
         ro, rl = oracle.decode(q, kc_h, vc_h, bt, cl, scale)
         assert_attention(out, lse, ro, rl, f"step {step} decode of {len(seqs)}")
