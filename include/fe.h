@@ -101,7 +101,12 @@ int fe_paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot
  * Bytes of device workspace fe_paged_gqa_decode needs for these sizes and
  * this num_partitions (0 = the automatic choice, which depends only on the
  * arguments here).  Host-only; returns 0 when no workspace is needed
- * (single partition) and (size_t)-1 for invalid sizes.
+ * (single partition) and (size_t)-1 for invalid sizes.  Hkv is an argument
+ * because the automatic choice fills the GPU with (sequence, KV head,
+ * partition) work items, whose count depends on it.
+ * Source: ForgeLM README, "Core Principles" 1 (a small hot path with
+ * controlled allocation: the caller sizes and owns the scratch memory); the
+ * workspace holds the split-K partials of fe_paged_gqa_decode.
  */
 size_t fe_paged_gqa_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_context_len,
                                           int num_partitions);
@@ -109,6 +114,7 @@ size_t fe_paged_gqa_decode_workspace_size(int B, int Hq, int Hkv, int D, int max
 /*
  * Number of KV partitions fe_paged_gqa_decode uses for these arguments
  * (num_partitions 0 = automatic).  Host-only; -1 for invalid sizes.
+ * Source: as fe_paged_gqa_decode_workspace_size.
  */
 int fe_paged_gqa_decode_num_partitions(int B, int Hq, int Hkv, int D, int max_context_len,
                                        int num_partitions);
@@ -230,6 +236,8 @@ int fe_paged_gqa_prefill_chunk_ex(void* out, float* lse, const void* q, const in
  * Bytes of device workspace fe_paged_gqa_mixed needs for these sizes
  * (num_partitions 0 = automatic).  Host-only; 0 when no decode sequence is
  * split, (size_t)-1 for invalid sizes.
+ * Source: ForgeLM README, "Core Principles" 1 (controlled allocation); the
+ * workspace holds the arrival counters and partials of fe_paged_gqa_mixed.
  */
 size_t fe_paged_gqa_mixed_workspace_size(int num_decode, int Hq, int Hkv, int D, int max_context_len,
                                          int num_partitions);
@@ -306,6 +314,8 @@ int fe_qk_norm_rope_append(void* q_out, const void* q, const void* k, const void
 /*
  * Bytes of device workspace fe_sampler_softmax_argmax needs for B rows of
  * V logits (host-only; (size_t)-1 for invalid sizes).
+ * Source: ForgeLM README, "Core Principles" 1 (controlled allocation); the
+ * workspace holds the per-range partials of fe_sampler_softmax_argmax.
  */
 size_t fe_sampler_workspace_size(int B, int V);
 
@@ -380,10 +390,22 @@ int fe_kv_allocator_num_allocated(const fe_kv_allocator* a);
 int fe_kv_allocator_batch(const fe_kv_allocator* a, const int* seqs, int n, int32_t* block_tables, int row_len,
                           int32_t pad_block, int32_t* context_lens);
 
-/* Static description of a status code (never NULL). */
+/*
+ * Static description of a status code (never NULL; "FE_ERR_UNKNOWN" for a
+ * value that is not an fe_status).
+ * Source: ForgeLM README, "Proposed Stack" (a C/C++ native backend reached
+ * through FFI bindings, across which errors travel as status codes, not
+ * exceptions); ForgeEngine README, "Verified L4 results" (parameter
+ * validation is part of what its tests check).
+ */
 const char* fe_status_string(int status);
 
-/* Detail of the most recent failure on the calling thread ("" if none). */
+/*
+ * Detail of the most recent failure on the calling thread ("" if none): the
+ * function, the argument or size that failed a check, or the HIP error text.
+ * Valid until the next failing call on the same thread.
+ * Source: as fe_status_string.
+ */
 const char* fe_last_error(void);
 
 #ifdef __cplusplus

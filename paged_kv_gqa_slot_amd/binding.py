@@ -122,14 +122,33 @@ def _dev(t: Optional[torch.Tensor], dtype, name: str, ndim: Optional[int] = None
     return t.data_ptr()
 
 
+def _shape(t: Optional[torch.Tensor], name: str, *dims):
+    """Raise ValueError unless t (if given) has exactly len(dims) dimensions
+    whose sizes equal dims (None matches any size).  Runs before any pointer
+    is passed on, so a mis-shaped tensor never reaches a kernel."""
+    if t is None:
+        return
+    shape = tuple(t.shape)
+    if len(shape) != len(dims) or any(d is not None and s != d for s, d in zip(shape, dims)):
+        want = "[" + "][".join("*" if d is None else str(d) for d in dims) + "]"
+        raise ValueError(f"{name}: expected shape {want}, got {list(shape)}")
+
+
+def _pools(k_cache, v_cache):
+    """(NB, Hkv, BS, D) of the K/V pools; both must be [NB][Hkv][BS][D] alike."""
+    _shape(k_cache, "k_cache", None, None, None, None)
+    _shape(v_cache, "v_cache", *k_cache.shape)
+    return tuple(k_cache.shape)
+
+
 def fe_paged_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
     """Scatter k_new/v_new [T][Hkv][D] into the pools [NB][Hkv][BS][D] by slot."""
-    NB, Hkv, BS, D = k_cache.shape
+    NB, Hkv, BS, D = _pools(k_cache, v_cache)
+    _shape(slot_mapping, "slot_mapping", None)
     T = slot_mapping.shape[0]
-    if tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("k_cache and v_cache shapes differ")
-    if T and (tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D)):
-        raise ValueError("k_new/v_new must be [T][Hkv][D]")
+    if T:
+        _shape(k_new, "k_new", T, Hkv, D)
+        _shape(v_new, "v_new", T, Hkv, D)
     rc = load_library().fe_paged_kv_append(
         _dev(k_new, torch.bfloat16, "k_new"), _dev(v_new, torch.bfloat16, "v_new"),
         _dev(slot_mapping, torch.int32, "slot_mapping", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
@@ -151,12 +170,24 @@ def fe_paged_gqa_decode_num_partitions(B, Hq, Hkv, D, max_context_len, num_parti
     return int(n)
 
 
+def _decode_shapes(out, lse, q, k_cache, block_tables, context_lens):
+    B, Hq, D = q.shape
+    _shape(out, "out", B, Hq, D)
+    _shape(lse, "lse", B, Hq)
+    _shape(block_tables, "block_tables", B, None)
+    _shape(context_lens, "context_lens", B)
+    if k_cache.shape[3] != D:
+        raise ValueError(f"q's head_dim {D} differs from the pools' {k_cache.shape[3]}")
+
+
 def fe_paged_gqa_decode(out, lse, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
                         scale: float, num_partitions: int = 0, workspace=None, stream=None) -> None:
     """Decode attention.  ``workspace`` is a uint8 device tensor of at least
     fe_paged_gqa_decode_workspace_size() bytes; one is allocated when not given."""
+    _shape(q, "q", None, None, None)
     B, Hq, D = q.shape
-    NB, Hkv, BS, _ = k_cache.shape
+    NB, Hkv, BS, _ = _pools(k_cache, v_cache)
+    _decode_shapes(out, lse, q, k_cache, block_tables, context_lens)
     ws_bytes = fe_paged_gqa_decode_workspace_size(B, Hq, Hkv, D, max_context_len, num_partitions)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
@@ -171,16 +202,48 @@ def fe_paged_gqa_decode(out, lse, q, k_cache, v_cache, block_tables, context_len
     _check(rc, "fe_paged_gqa_decode")
 
 
+def check_decode_append_slots(slot_mapping, block_tables, context_lens, num_blocks: int, block_size: int,
+                              max_context_len: int) -> None:
+    """Host-side check of fe_paged_gqa_decode_append's precondition: for
+    every sequence b with L = min(context_lens[b], max_context_len,
+    block_tables row length * block_size) > 0 whose slot lies in the pool,
+    slot_mapping[b] == block_tables[b][(L-1) // BS] * BS + (L-1) % BS.
+    Raises ValueError naming the first offending sequence.  Takes torch
+    tensors (device or host) or arrays; device ones are copied to the host."""
+    sm = np.asarray(slot_mapping.cpu() if hasattr(slot_mapping, "cpu") else slot_mapping, dtype=np.int64)
+    bt = np.asarray(block_tables.cpu() if hasattr(block_tables, "cpu") else block_tables, dtype=np.int64)
+    cl = np.asarray(context_lens.cpu() if hasattr(context_lens, "cpu") else context_lens, dtype=np.int64)
+    cap = min(int(max_context_len), bt.shape[1] * block_size)
+    for b in range(sm.shape[0]):
+        L = min(max(int(cl[b]), 0), cap)
+        s = int(sm[b])
+        if L == 0 or s < 0 or s >= num_blocks * block_size:
+            continue
+        want = int(bt[b, (L - 1) // block_size]) * block_size + (L - 1) % block_size
+        if s != want:
+            raise ValueError(f"slot_mapping[{b}] = {s} is not the slot of position {L - 1} "
+                             f"(block_tables gives {want})")
+
+
 def fe_paged_gqa_decode_append(out, lse, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
                                max_context_len: int, scale: float, num_partitions: int = 0, workspace=None,
-                               stream=None) -> None:
+                               stream=None, validate: bool = False) -> None:
     """Append of one new K/V row per sequence (into slot_mapping[b], the
     slot of position context_lens[b] - 1) fused into decode attention.
-    Same workspace as fe_paged_gqa_decode; one is allocated when not given."""
+    Same workspace as fe_paged_gqa_decode; one is allocated when not given.
+
+    validate=True first checks the call's precondition on host copies (a
+    device synchronisation): every in-pool slot_mapping[b] must be the slot
+    of position context_lens[b] - 1 in row b of block_tables."""
+    _shape(q, "q", None, None, None)
     B, Hq, D = q.shape
-    NB, Hkv, BS, _ = k_cache.shape
-    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D) or tuple(slot_mapping.shape) != (B,):
-        raise ValueError("k_new/v_new must be [B][Hkv][D] and slot_mapping [B]")
+    NB, Hkv, BS, _ = _pools(k_cache, v_cache)
+    _decode_shapes(out, lse, q, k_cache, block_tables, context_lens)
+    _shape(k_new, "k_new", B, Hkv, D)
+    _shape(v_new, "v_new", B, Hkv, D)
+    _shape(slot_mapping, "slot_mapping", B)
+    if validate:
+        check_decode_append_slots(slot_mapping, block_tables, context_lens, NB, BS, max_context_len)
     ws_bytes = fe_paged_gqa_decode_workspace_size(B, Hq, Hkv, D, max_context_len, num_partitions)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
@@ -196,12 +259,25 @@ def fe_paged_gqa_decode_append(out, lse, q, k_new, v_new, slot_mapping, k_cache,
     _check(rc, "fe_paged_gqa_decode_append")
 
 
+def _packed_shapes(out, lse, q, query_start_loc, k_cache, block_tables, B):
+    total_q, Hq, D = q.shape
+    _shape(out, "out", total_q, Hq, D)
+    _shape(lse, "lse", total_q, Hq)
+    _shape(query_start_loc, "query_start_loc", B + 1)
+    _shape(block_tables, "block_tables", B, None)
+    if k_cache.shape[3] != D:
+        raise ValueError(f"q's head_dim {D} differs from the pools' {k_cache.shape[3]}")
+
+
 def fe_paged_gqa_prefill_chunk(out, lse, q, query_start_loc, k_cache, v_cache, block_tables, context_lens,
                                max_q_len: int, max_context_len: int, scale: float, stream=None) -> None:
     """Chunked prefill attention over the paged cache (bottom-right causal)."""
+    _shape(q, "q", None, None, None)
     total_q, Hq, D = q.shape
-    NB, Hkv, BS, _ = k_cache.shape
+    NB, Hkv, BS, _ = _pools(k_cache, v_cache)
+    _shape(context_lens, "context_lens", None)
     B = context_lens.shape[0]
+    _packed_shapes(out, lse, q, query_start_loc, k_cache, block_tables, B)
     rc = load_library().fe_paged_gqa_prefill_chunk(
         _dev(out, torch.bfloat16, "out", 3), _dev(lse, torch.float32, "lse", 2), _dev(q, torch.bfloat16, "q", 3),
         _dev(query_start_loc, torch.int32, "query_start_loc", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
@@ -216,9 +292,12 @@ def fe_paged_gqa_prefill_chunk_ex(out, lse, q, query_start_loc, k_cache, v_cache
                                   stream=None) -> None:
     """fe_paged_gqa_prefill_chunk with the tile shape chosen by the caller
     (key_groups 0 automatic, 1 or 2 wave groups per workgroup)."""
+    _shape(q, "q", None, None, None)
     total_q, Hq, D = q.shape
-    NB, Hkv, BS, _ = k_cache.shape
+    NB, Hkv, BS, _ = _pools(k_cache, v_cache)
+    _shape(context_lens, "context_lens", None)
     B = context_lens.shape[0]
+    _packed_shapes(out, lse, q, query_start_loc, k_cache, block_tables, B)
     rc = load_library().fe_paged_gqa_prefill_chunk_ex(
         _dev(out, torch.bfloat16, "out", 3), _dev(lse, torch.float32, "lse", 2), _dev(q, torch.bfloat16, "q", 3),
         _dev(query_start_loc, torch.int32, "query_start_loc", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
@@ -242,9 +321,12 @@ def fe_paged_gqa_mixed(out, lse, q, query_start_loc, k_cache, v_cache, block_tab
     chunks (the rest) in one launch.  ``workspace``: uint8 device tensor of at
     least fe_paged_gqa_mixed_workspace_size() bytes, zero-filled before its
     first use; one is allocated (zeroed) when not given."""
+    _shape(q, "q", None, None, None)
     total_q, Hq, D = q.shape
-    NB, Hkv, BS, _ = k_cache.shape
+    NB, Hkv, BS, _ = _pools(k_cache, v_cache)
+    _shape(context_lens, "context_lens", None)
     B = context_lens.shape[0]
+    _packed_shapes(out, lse, q, query_start_loc, k_cache, block_tables, B)
     ws_bytes = fe_paged_gqa_mixed_workspace_size(num_decode, Hq, Hkv, D, max_context_len, num_partitions)
     if workspace is None and ws_bytes:
         workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
@@ -264,12 +346,17 @@ def fe_qk_norm_rope_append(q_out, q, k, v, q_norm_w, k_norm_w, cos_sin, position
                            eps: float, stream=None) -> None:
     """Per-head RMSNorm + rotary embedding of q and k, then append of k and v
     into the pools; q_out may be q (in place)."""
+    _shape(q, "q", None, None, None)
     T, Hq, D = q.shape
-    NB, Hkv, BS, _ = k_cache.shape
-    if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D) or tuple(q_out.shape) != (T, Hq, D):
-        raise ValueError("q/q_out must be [T][Hq][D] and k/v [T][Hkv][D]")
-    if cos_sin.dim() != 2 or cos_sin.shape[1] != D:
-        raise ValueError("cos_sin must be [max_pos][D]")
+    NB, Hkv, BS, _ = _pools(k_cache, v_cache)
+    _shape(q_out, "q_out", T, Hq, D)
+    _shape(k, "k", T, Hkv, D)
+    _shape(v, "v", T, Hkv, D)
+    _shape(cos_sin, "cos_sin", None, D)
+    _shape(q_norm_w, "q_norm_w", D)
+    _shape(k_norm_w, "k_norm_w", D)
+    _shape(positions, "positions", T)
+    _shape(slot_mapping, "slot_mapping", T)
     rc = load_library().fe_qk_norm_rope_append(
         _dev(q_out, torch.bfloat16, "q_out", 3), _dev(q, torch.bfloat16, "q", 3), _dev(k, torch.bfloat16, "k", 3),
         _dev(v, torch.bfloat16, "v", 3), _dev(q_norm_w, torch.bfloat16, "q_norm_w", 1),
@@ -289,7 +376,12 @@ def fe_sampler_workspace_size(B: int, V: int) -> int:
 
 def fe_sampler_softmax_argmax(probs, lse, argmax, logits, inv_temperature=None, workspace=None, stream=None) -> None:
     """fp32 softmax (probs may be None), LSE (may be None) and greedy argmax of bf16 logits [B][V]."""
+    _shape(logits, "logits", None, None)
     B, V = logits.shape
+    _shape(probs, "probs", B, V)
+    _shape(lse, "lse", B)
+    _shape(argmax, "argmax", B)
+    _shape(inv_temperature, "inv_temperature", B)
     ws_bytes = fe_sampler_workspace_size(B, V)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=logits.device)

@@ -311,3 +311,158 @@ def test_oversized_launches_rejected(lib):
     assert pre(lib, mql=1 << 30, B=1 << 10, tq=1 << 30) == UNSUPPORTED
     assert nr(lib, T=1 << 28) == UNSUPPORTED
     assert "2^32" in fe.fe_last_error()
+
+
+# -- host-side shape checks of the Python binding: a mis-shaped tensor is
+# rejected before any pointer reaches the library (CPU tensors suffice, since
+# the shape check comes before the device check) ------------------------------
+
+def _bf(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def _i32(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.int32)
+
+
+def _f32(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.float32)
+
+
+def _decode_args(B=2, Hq=8, Hkv=2, NB=16, mb=4):
+    return dict(out=_bf(B, Hq, 128), lse=_f32(B, Hq), q=_bf(B, Hq, 128), k_cache=_bf(NB, Hkv, 16, 128),
+                v_cache=_bf(NB, Hkv, 16, 128), block_tables=_i32(B, mb), context_lens=_i32(B))
+
+
+@pytest.mark.parametrize("bad, pattern", [
+    (dict(out=_bf(2, 8, 64)), "out"),
+    (dict(out=_bf(3, 8, 128)), "out"),
+    (dict(lse=_f32(2, 4)), "lse"),
+    (dict(context_lens=_i32(3)), "context_lens"),
+    (dict(block_tables=_i32(1, 4)), "block_tables"),
+    (dict(block_tables=_i32(8)), "block_tables"),
+    (dict(v_cache=_bf(8, 2, 16, 128)), "v_cache"),
+    (dict(k_cache=_bf(16, 2, 16, 64), v_cache=_bf(16, 2, 16, 64)), "head_dim"),
+])
+def test_binding_rejects_misshaped_decode(lib, bad, pattern):
+    a = _decode_args()
+    a.update(bad)
+    with pytest.raises(ValueError, match=pattern):
+        fe.fe_paged_gqa_decode(a["out"], a["lse"], a["q"], a["k_cache"], a["v_cache"], a["block_tables"],
+                               a["context_lens"], 64, 0.088, num_partitions=1)
+
+
+@pytest.mark.parametrize("bad, pattern", [
+    (dict(out=_bf(2, 4, 128)), "out"),
+    (dict(context_lens=_i32(1)), "context_lens"),
+    (dict(v_cache=_bf(16, 1, 16, 128)), "v_cache"),
+    (dict(k_new=_bf(2, 1, 128)), "k_new"),
+    (dict(v_new=_bf(3, 2, 128)), "v_new"),
+    (dict(slot_mapping=_i32(5)), "slot_mapping"),
+])
+def test_binding_rejects_misshaped_decode_append(lib, bad, pattern):
+    a = _decode_args()
+    a.update(k_new=_bf(2, 2, 128), v_new=_bf(2, 2, 128), slot_mapping=_i32(2))
+    a.update(bad)
+    with pytest.raises(ValueError, match=pattern):
+        fe.fe_paged_gqa_decode_append(a["out"], a["lse"], a["q"], a["k_new"], a["v_new"], a["slot_mapping"],
+                                      a["k_cache"], a["v_cache"], a["block_tables"], a["context_lens"], 64, 0.088,
+                                      num_partitions=1)
+
+
+def _packed_args(B=2, tq=10, Hq=8, Hkv=2, NB=16, mb=4):
+    return dict(out=_bf(tq, Hq, 128), lse=_f32(tq, Hq), q=_bf(tq, Hq, 128), qsl=_i32(B + 1),
+                k_cache=_bf(NB, Hkv, 16, 128), v_cache=_bf(NB, Hkv, 16, 128), block_tables=_i32(B, mb),
+                context_lens=_i32(B))
+
+
+@pytest.mark.parametrize("bad, pattern", [
+    (dict(out=_bf(9, 8, 128)), "out"),
+    (dict(lse=_f32(10, 2)), "lse"),
+    (dict(qsl=_i32(2)), "query_start_loc"),
+    (dict(block_tables=_i32(3, 4)), "block_tables"),
+    (dict(v_cache=_bf(16, 2, 8, 128)), "v_cache"),
+])
+@pytest.mark.parametrize("call", ["prefill", "prefill_ex", "mixed"])
+def test_binding_rejects_misshaped_packed(lib, bad, pattern, call):
+    a = _packed_args()
+    a.update(bad)
+    args = (a["out"], a["lse"], a["q"], a["qsl"], a["k_cache"], a["v_cache"], a["block_tables"], a["context_lens"])
+    with pytest.raises(ValueError, match=pattern):
+        if call == "prefill":
+            fe.fe_paged_gqa_prefill_chunk(*args, 8, 64, 0.088)
+        elif call == "prefill_ex":
+            fe.fe_paged_gqa_prefill_chunk_ex(*args, 8, 64, 0.088, 1)
+        else:
+            fe.fe_paged_gqa_mixed(*args, 1, 8, 64, 0.088, num_partitions=1, workspace=torch_uint8(16))
+
+
+def torch_uint8(n):
+    import torch
+    return torch.zeros(n, dtype=torch.uint8)
+
+
+@pytest.mark.parametrize("bad, pattern", [
+    (dict(probs=_f32(4, 1000)), "probs"),
+    (dict(lse=_f32(3)), "lse"),
+    (dict(argmax=_i32(5)), "argmax"),
+    (dict(inv_temperature=_f32(2)), "inv_temperature"),
+])
+def test_binding_rejects_misshaped_sampler(lib, bad, pattern):
+    a = dict(probs=_f32(4, 1024), lse=_f32(4), argmax=_i32(4), logits=_bf(4, 1024), inv_temperature=_f32(4))
+    a.update(bad)
+    with pytest.raises(ValueError, match=pattern):
+        fe.fe_sampler_softmax_argmax(a["probs"], a["lse"], a["argmax"], a["logits"], a["inv_temperature"],
+                                     workspace=torch_uint8(1 << 16))
+
+
+@pytest.mark.parametrize("bad, pattern", [
+    (dict(q_out=_bf(2, 8, 128)), "q_out"),
+    (dict(positions=_i32(2)), "positions"),
+    (dict(slot_mapping=_i32(4)), "slot_mapping"),
+    (dict(q_norm_w=_bf(64)), "q_norm_w"),
+    (dict(cos_sin=_f32(32, 64)), "cos_sin"),
+    (dict(v_cache=_bf(8, 2, 16, 128)), "v_cache"),
+])
+def test_binding_rejects_misshaped_norm_rope(lib, bad, pattern):
+    a = dict(q_out=_bf(3, 8, 128), q=_bf(3, 8, 128), k=_bf(3, 2, 128), v=_bf(3, 2, 128), q_norm_w=_bf(128),
+             k_norm_w=_bf(128), cos_sin=_f32(32, 128), positions=_i32(3), slot_mapping=_i32(3),
+             k_cache=_bf(16, 2, 16, 128), v_cache=_bf(16, 2, 16, 128))
+    a.update(bad)
+    with pytest.raises(ValueError, match=pattern):
+        fe.fe_qk_norm_rope_append(a["q_out"], a["q"], a["k"], a["v"], a["q_norm_w"], a["k_norm_w"], a["cos_sin"],
+                                  a["positions"], a["slot_mapping"], a["k_cache"], a["v_cache"], 1e-6)
+
+
+def test_binding_rejects_misshaped_append(lib):
+    with pytest.raises(ValueError, match="k_new"):
+        fe.fe_paged_kv_append(_bf(3, 1, 128), _bf(3, 2, 128), _i32(3), _bf(16, 2, 16, 128), _bf(16, 2, 16, 128))
+    with pytest.raises(ValueError, match="v_cache"):
+        fe.fe_paged_kv_append(_bf(3, 2, 128), _bf(3, 2, 128), _i32(3), _bf(16, 2, 16, 128), _bf(16, 4, 16, 128))
+    with pytest.raises(ValueError, match="slot_mapping"):
+        fe.fe_paged_kv_append(_bf(3, 2, 128), _bf(3, 2, 128), _i32(3, 1), _bf(16, 2, 16, 128), _bf(16, 2, 16, 128))
+
+
+def test_decode_append_slot_precondition_check():
+    """check_decode_append_slots (the validate=True path of
+    fe_paged_gqa_decode_append) accepts the slot of each sequence's last
+    position, padding, out-of-pool slots and empty sequences, and names the
+    first sequence whose in-pool slot is anywhere else."""
+    import numpy as np
+    bt = np.array([[5, 2, 9], [7, 1, 0], [3, 4, 6]], np.int32)
+    lens = np.array([20, 16, 0], np.int32)  # positions 19 (block 2, row 3) and 15 (block 7, row 15)
+    good = np.array([2 * 16 + 3, 7 * 16 + 15, 123], np.int32)
+    binding.check_decode_append_slots(good, bt, lens, 10, 16, 48)
+    binding.check_decode_append_slots(np.array([-1, 7 * 16 + 15, 0], np.int32), bt, lens, 10, 16, 48)
+    binding.check_decode_append_slots(np.array([10 * 16, -5, 0], np.int32), bt, lens, 10, 16, 48)  # past the pool
+    with pytest.raises(ValueError, match=r"slot_mapping\[0\]"):
+        binding.check_decode_append_slots(np.array([2 * 16 + 2, 7 * 16 + 15, 0], np.int32), bt, lens, 10, 16, 48)
+    with pytest.raises(ValueError, match=r"slot_mapping\[1\]"):
+        binding.check_decode_append_slots(np.array([2 * 16 + 3, 1 * 16, 0], np.int32), bt, lens, 10, 16, 48)
+    # the context is clamped as the kernel clamps it: max_context_len 16 puts
+    # sequence 0's last position at 15 (block 5, row 15)
+    binding.check_decode_append_slots(np.array([5 * 16 + 15, 7 * 16 + 15, 0], np.int32), bt, lens, 10, 16, 16)
+

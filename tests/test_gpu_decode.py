@@ -143,21 +143,23 @@ def test_decode_qwen3_0_6b_b1_ctx128(dev, seed):
     run_decode(w, dev, parts=(0, 1, 2, 8), label=f"0.6b b1 seed {seed}")
 
 
-def test_decode_qwen3_4b_b4_36layers(dev):
-    w = inputs.make("qwen3_4b_b4_ctx256-2048_36layers", poison="nan")
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_decode_qwen3_4b_b4_36layers(dev, seed):
+    w = inputs.make("qwen3_4b_b4_ctx256-2048_36layers", seed=seed, poison="nan")
     for layer in range(len(w.layers)):
-        run_decode(w, dev, parts=(0,), label=f"4b b4 layer {layer}", layer=layer)
+        run_decode(w, dev, parts=(0,), label=f"4b b4 seed {seed} layer {layer}", layer=layer)
 
 
-@pytest.mark.parametrize("seed", [3, 4])
+@pytest.mark.parametrize("seed", [1, 2, 3])
 def test_decode_qwen3_4b_b64(dev, seed):
     w = inputs.make("qwen3_4b_b64_ctx1024-8192", seed=seed, poison="nan")
     run_decode(w, dev, parts=(0, 1, 16), label=f"4b b64 seed {seed}")
 
 
-def test_decode_qwen3_4b_b8_ctx32768(dev):
-    w = inputs.make("qwen3_4b_b8_ctx32768", poison="nan")
-    run_decode(w, dev, parts=(8, 16, 32, 0), label="4b b8 32k")
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_decode_qwen3_4b_b8_ctx32768(dev, seed):
+    w = inputs.make("qwen3_4b_b8_ctx32768", seed=seed, poison="nan")
+    run_decode(w, dev, parts=(8, 16, 32, 0), label=f"4b b8 32k seed {seed}")
 
 
 def test_decode_workspace_reuse(dev):
@@ -258,7 +260,7 @@ def test_decode_append_padding_and_out_of_range_slots(dev):
     run_decode_append(w, dev, parts=(1, 0), label="fused padding", slots_override=slots, pre=pre)
 
 
-@pytest.mark.parametrize("seed", [3, 4])
+@pytest.mark.parametrize("seed", [1, 2, 3])
 def test_decode_append_qwen3_4b_b64(dev, seed):
     """The serving-concurrency workload, its append fused into the decode call."""
     w = inputs.make("qwen3_4b_b64_ctx1024-8192", seed=seed, poison="nan")

@@ -6,7 +6,7 @@ chunked-prefill definition covers every row of a mixed batch.  Cases: small
 ragged batches for several group sizes and split-K factors with NaN/large
 poison (decode rows with empty, partial-block and multi-partition contexts),
 batches that are all decode or all prefill, workspace reuse, and the full
-Qwen3-4B mixed step on sampled rows.  Gate: max-abs 1e-2, row-relative 1e-2,
+Qwen3-4B mixed step on every row.  Gate: max-abs 1e-2, row-relative 1e-2,
 LSE 1e-3.
 """
 import pytest
@@ -100,8 +100,6 @@ def test_mixed_workspace_reuse(dev):
 @pytest.mark.parametrize("seed", [7])
 def test_mixed_qwen3_4b_step(dev, seed):
     """The full mixed step (60 decode rows of 1024..8192 tokens and 4 chunks of
-    256 after 4096 cached tokens) on every decode row and sampled prefill rows."""
+    256 after 4096 cached tokens) on every row."""
     w = inputs.make("qwen3_4b_mixed_dec60_ctx1024-8192_pre4_prefix4096_chunk256", seed=seed, poison="nan")
-    total_q = int(w.query_start_loc[-1])
-    rows = sorted(set(list(range(60)) + list(range(60, total_q, 9)) + [60, 315, 316, total_q - 1]))
-    run_mixed(w, dev, parts=(0, 16), label=f"mixed 4b step seed {seed}", rows=rows)
+    run_mixed(w, dev, parts=(0, 16), label=f"mixed 4b step seed {seed}")

@@ -4,7 +4,7 @@ Cases go through the C ABI on cuda:0: small ragged chunks spanning several
 64-key tiles and 32-query tiles with NaN/large poison, every group size, a
 context shorter than its chunk (rows with no visible key), the hand-derived
 golden example, prefill rows against the decode kernel, and the full 4 x
-(4096 + 256) Qwen3-4B workload on sampled rows.  Gate: max-abs 1e-2,
+(4096 + 256) and 64 x (1024 + 256) Qwen3-4B workloads on every row.  Gate: max-abs 1e-2,
 row-relative 1e-2, LSE 1e-3.
 """
 import json
@@ -230,16 +230,13 @@ def test_prefill_golden(dev):
 
 def test_prefill_qwen3_4b_b64_prefix1024_chunk256(dev):
     """The 64 x (1024 + 256) step: 4096 workgroups, so the automatic call
-    runs one key group per workgroup; sampled rows cover every sequence."""
+    runs one key group per workgroup; every one of its 16384 rows."""
     w = inputs.make("qwen3_4b_b64_prefix1024_chunk256", poison="nan")
-    total_q = int(w.query_start_loc[-1])
-    rows = sorted(set(list(range(0, total_q, 37)) + [0, 255, 256, total_q - 1]))
-    run_prefill(w, dev, "prefill 4b b64 prefix 1024", rows=rows)
+    run_prefill(w, dev, "prefill 4b b64 prefix 1024")
 
 
-@pytest.mark.parametrize("seed", [5, 6])
+@pytest.mark.parametrize("seed", [1, 2, 3])
 def test_prefill_qwen3_4b_b4_prefix4096_chunk256(dev, seed):
+    """The chunked-prefill workload (4 x (4096 + 256)) on all 1024 rows."""
     w = inputs.make("qwen3_4b_b4_prefix4096_chunk256", seed=seed, poison="nan")
-    total_q = int(w.query_start_loc[-1])
-    rows = sorted(set(list(range(0, total_q, 7)) + [0, 31, 32, 255, 256, 511, total_q - 1]))
-    run_prefill(w, dev, f"prefill 4b b4 seed {seed}", rows=rows)
+    run_prefill(w, dev, f"prefill 4b b4 seed {seed}")
