@@ -154,6 +154,34 @@ int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cach
                         hipStream_t stream);
 
 /*
+ * fe_paged_gqa_decode without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   Every argument, the result and the errors are those of
+ *   fe_paged_gqa_decode (same kernels, same partitioning, bit-identical
+ *   results), except that the split-K partials live in a device array of
+ *   32 MiB inside the library: one copy per GPU, created with the code
+ *   object and held until the process ends.  Its address on a device is
+ *   looked up once (with that device current) on the first call for it.
+ *   Sizes whose workspace (fe_paged_gqa_decode_workspace_size) exceeds
+ *   32 MiB return FE_ERR_WORKSPACE before anything is enqueued; lower
+ *   num_partitions or use fe_paged_gqa_decode.  Single-partition calls use
+ *   no scratch at all.
+ *   Every call on one GPU shares that GPU's array, and a call leaves its
+ *   partials there: two calls that may overlap in time on one GPU (different
+ *   streams, or graphs replayed concurrently) race on it and give
+ *   unspecified results.  Calls ordered on one stream are safe.  The array
+ *   needs no initialisation (every partial is written before it is read).
+ *   A failed device lookup returns FE_ERR_HIP.
+ * For callers that cannot allocate; the operation is that of
+ * fe_paged_gqa_decode.
+ */
+int fe_paged_gqa_decode_noalloc(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                                int B, int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len,
+                                float scale, int num_partitions, hipStream_t stream);
+
+/*
  * fe_paged_kv_append of one new token per sequence fused into
  * fe_paged_gqa_decode: one launch instead of two for the per-token step
  * (append the token's K/V, then attend over the context that ends with it).

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     fe_last_error,
     fe_paged_gqa_decode,
     fe_paged_gqa_decode_append,
+    fe_paged_gqa_decode_noalloc,
     fe_paged_gqa_decode_num_partitions,
     fe_paged_gqa_decode_workspace_size,
     fe_paged_gqa_mixed,

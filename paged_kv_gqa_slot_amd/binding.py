@@ -49,6 +49,8 @@ def load_library():
     lib.fe_paged_gqa_decode_num_partitions.restype = I
     lib.fe_paged_gqa_decode.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fe_paged_gqa_decode.restype = I
+    lib.fe_paged_gqa_decode_noalloc.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P]
+    lib.fe_paged_gqa_decode_noalloc.restype = I
     lib.fe_paged_gqa_decode_append.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fe_paged_gqa_decode_append.restype = I
     lib.fe_paged_gqa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, P]
@@ -200,6 +202,24 @@ def fe_paged_gqa_decode(out, lse, q, k_cache, v_cache, block_tables, context_len
         _dev(context_lens, torch.int32, "context_lens", 1), B, Hq, Hkv, D, BS, NB, int(max_context_len),
         float(scale), int(num_partitions), ws_ptr, ws_have, _stream(stream))
     _check(rc, "fe_paged_gqa_decode")
+
+
+def fe_paged_gqa_decode_noalloc(out, lse, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                                scale: float, num_partitions: int = 0, stream=None) -> None:
+    """fe_paged_gqa_decode with no workspace and no allocation: the split-K
+    partials live in the library's per-GPU device scratch (32 MiB).  Calls
+    that may overlap in time on one GPU race on that scratch."""
+    _shape(q, "q", None, None, None)
+    B, Hq, D = q.shape
+    NB, Hkv, BS, _ = _pools(k_cache, v_cache)
+    _decode_shapes(out, lse, q, k_cache, block_tables, context_lens)
+    rc = load_library().fe_paged_gqa_decode_noalloc(
+        _dev(out, torch.bfloat16, "out", 3), _dev(lse, torch.float32, "lse", 2), _dev(q, torch.bfloat16, "q", 3),
+        _dev(k_cache, torch.bfloat16, "k_cache", 4), _dev(v_cache, torch.bfloat16, "v_cache", 4),
+        _dev(block_tables, torch.int32, "block_tables", 2), block_tables.shape[1],
+        _dev(context_lens, torch.int32, "context_lens", 1), B, Hq, Hkv, D, BS, NB, int(max_context_len),
+        float(scale), int(num_partitions), _stream(stream))
+    _check(rc, "fe_paged_gqa_decode_noalloc")
 
 
 def check_decode_append_slots(slot_mapping, block_tables, context_lens, num_blocks: int, block_size: int,

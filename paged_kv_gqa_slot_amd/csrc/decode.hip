@@ -13,7 +13,14 @@
 // holds the sequence's last block.
 #include <math.h>
 
+#include <mutex>
+
 #include "decode_body.h"
+
+// Split-K workspace of the allocation-free decode call, one copy per GPU,
+// held until the process ends.  Host code never uses this name as an
+// address: decode_scratch() looks the device address up per device.
+static __device__ __align__(256) unsigned char scratch[fe::kDecodeScratchBytes];
 
 namespace fe {
 namespace {
@@ -146,6 +153,37 @@ bool plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_partitions
   }
   *plan = r;
   return true;
+}
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // the array's address on device `dev`, looked up with that device current
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -108,7 +108,7 @@ int decode_call(const char* fn, void* out, float* lse, const void* q, const void
                 const int32_t* slot_mapping, bool fused, const void* k_cache, const void* v_cache,
                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens, int B, int Hq,
                 int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale, int num_partitions,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                void* workspace, size_t workspace_bytes, hipStream_t stream, bool use_scratch = false) {
   try {
     if (B < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_partitions < 0)
       return fail(FE_ERR_INVALID_ARG, fn,
@@ -126,12 +126,26 @@ int decode_call(const char* fn, void* out, float* lse, const void* q, const void
     fe::DecodePlan plan;
     if (!fe::plan_decode(B, Hq, Hkv, max_context_len, num_partitions, &plan))
       return fail(FE_ERR_INVALID_ARG, fn, "cannot plan these sizes");
-    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    if (use_scratch) {
+      if (plan.workspace_bytes > fe::kDecodeScratchBytes) {
+        char msg[384];
+        std::snprintf(msg, sizeof msg,
+                      "these sizes need %zu bytes of split-K workspace, above the %zu bytes of device scratch the "
+                      "allocation-free call holds (use fe_paged_gqa_decode with a workspace, or fewer partitions)",
+                      plan.workspace_bytes, fe::kDecodeScratchBytes);
+        return fail(FE_ERR_WORKSPACE, fn, msg);
+      }
+    } else if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes)) {
       return fail(FE_ERR_WORKSPACE, fn, "workspace missing or smaller than fe_paged_gqa_decode_workspace_size()");
+    }
     if (B == 0) return FE_OK;
     if (!launch_fits(static_cast<double>(B) * plan.partitions * Hkv, 256) ||
         !launch_fits(static_cast<double>(B) * Hq / 4, 256))
       return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
+    if (use_scratch && plan.workspace_bytes > 0) {
+      const hipError_t e = fe::decode_scratch(stream, &workspace);
+      if (e != hipSuccess) return hip_fail(e, fn);
+    }
     fe::DecodeArgs a{out, lse, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv,
                      num_blocks, max_context_len, scale, plan, workspace};
     if (fused) {
@@ -155,6 +169,15 @@ int fe_paged_gqa_decode(void* out, float* lse, const void* q, const void* k_cach
   return decode_call("fe_paged_gqa_decode", out, lse, q, nullptr, nullptr, nullptr, false, k_cache, v_cache,
                      block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, num_blocks, max_context_len,
                      scale, num_partitions, workspace, workspace_bytes, stream);
+}
+
+int fe_paged_gqa_decode_noalloc(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                                int B, int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len,
+                                float scale, int num_partitions, hipStream_t stream) {
+  return decode_call("fe_paged_gqa_decode_noalloc", out, lse, q, nullptr, nullptr, nullptr, false, k_cache, v_cache,
+                     block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, num_blocks, max_context_len,
+                     scale, num_partitions, nullptr, 0, stream, true);
 }
 
 int fe_paged_gqa_decode_append(void* out, float* lse, const void* q, const void* k_new, const void* v_new,

@@ -29,6 +29,13 @@ constexpr int kMaxPartBlocks = 256;
 // Returns false for sizes the decode kernel cannot plan (non-positive sizes).
 bool plan_decode(int B, int Hq, int Hkv, int max_context_len, int num_partitions, DecodePlan* plan);
 
+// Allocation-free decode (fe_paged_gqa_decode_noalloc): the split-K
+// workspace is a file-scope device array of this many bytes in decode.hip,
+// one copy per GPU.  decode_scratch() returns its address on the device of
+// `stream` (looked up once per device, then cached).
+constexpr size_t kDecodeScratchBytes = static_cast<size_t>(32) << 20;
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
+
 struct DecodeArgs {
   void* out;
   float* lse;

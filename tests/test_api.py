@@ -466,3 +466,30 @@ def test_decode_append_slot_precondition_check():
     # sequence 0's last position at 15 (block 5, row 15)
     binding.check_decode_append_slots(np.array([5 * 16 + 15, 7 * 16 + 15, 0], np.int32), bt, lens, 10, 16, 16)
 
+
+def dec_noalloc(lib, **kw):
+    a = dict(out=P, lse=None, q=P, k=P, v=P, bt=P, mb=8, cl=P, B=2, Hq=32, Hkv=8, D=128, BS=16, NB=64, mcl=128,
+             scale=0.088, parts=1, stream=None)
+    a.update(kw)
+    return lib.fe_paged_gqa_decode_noalloc(a["out"], a["lse"], a["q"], a["k"], a["v"], a["bt"], a["mb"], a["cl"],
+                                           a["B"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["NB"], a["mcl"], a["scale"],
+                                           a["parts"], a["stream"])
+
+
+def test_decode_noalloc_argument_errors(lib):
+    """The allocation-free decode checks what fe_paged_gqa_decode checks and
+    refuses, before anything is enqueued, sizes whose split-K partials do not
+    fit its 32 MiB of device scratch."""
+    assert dec_noalloc(lib, q=None) == NULL
+    assert dec_noalloc(lib, Hq=30) == INVALID
+    assert dec_noalloc(lib, scale=float("nan")) == INVALID
+    assert dec_noalloc(lib, D=64) == UNSUPPORTED
+    assert dec_noalloc(lib, q=P + 8) == INVALID
+    assert dec_noalloc(lib, B=0) == OK
+    ws = lib.fe_paged_gqa_decode_workspace_size
+    # 1024 sequences x 32 heads x 8 partitions of fp32 partials: 128 MiB
+    assert ws(1024, 32, 8, 128, 8192, 8) > (32 << 20)
+    assert dec_noalloc(lib, B=1024, mcl=8192, mb=512, parts=8) == WORKSPACE
+    assert "32" in fe.fe_last_error() and "scratch" in fe.fe_last_error()
+    # the gate-sized call fits (64 x 32 heads x 8 partitions: ~8.5 MB)
+    assert ws(64, 32, 8, 128, 8192, 0) <= (32 << 20)
