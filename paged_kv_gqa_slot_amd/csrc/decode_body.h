@@ -17,9 +17,9 @@
 //   16 lanes of a row.  Each row keeps its own online-softmax state (running
 //   max m, sum l, acc[G][8]) in the log2 domain; the max is only raised when
 //   it grows by more than 8 (so exp2 stays <= 256 and the rescale of acc is
-//   rare).  PV: v_dot2_f32_bf16 with the softmax weights of two tokens
-//   packed as a bf16 pair against the matching V words (fp32
-//   accumulation).  A partially filled last block is handled after the main
+//   rare).  PV in fp32: each V element is widened from bf16 (exact) and
+//   accumulated with the fp32 softmax weight by one fma, so the weights that
+//   enter the numerator are the ones summed into l.  A partially filled last block is handled after the main
 //   loop by a masked variant of the same step; with a fused append the last
 //   block always goes that way, and there the new token's row is written to
 //   the cache and patched into the loaded tile.
@@ -182,32 +182,28 @@ __device__ __forceinline__ void consume(State<G>& st, const Tile& t, const uint3
       }
     }
   }
-  // p = 2^(s * scale_log2 - m); the PV product takes p in bf16 pairs
-  // (tokens r + 8 u and r + 8 u + 4 share a pair) with fp32 accumulation
-  uint32_t pp[2][G];
+  // p = 2^(s * scale_log2 - m)
+  // PV in fp32: acc += p * v, v widened from bf16 (exact), one fma per
+  // (token, dim, head); the same p enters l and the numerator.
+  float pf[4][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float p[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = fast_exp2(fmaf(s[j][h], scale_log2, -st.m[h]));
-    st.l[h] += (p[0] + p[1]) + (p[2] + p[3]);
-    pp[0][h] = pack_bf16x2(p[0], p[1]);
-    pp[1][h] = pack_bf16x2(p[2], p[3]);
+    for (int j = 0; j < 4; ++j) pf[j][h] = fast_exp2(fmaf(s[j][h], scale_log2, -st.m[h]));
+    st.l[h] += (pf[0][h] + pf[1][h]) + (pf[2][h] + pf[3][h]);
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    uint32_t va[4], vb[4];
-    words4(t.v[2 * u], va);
-    words4(t.v[2 * u + 1], vb);
+  for (int j = 0; j < 4; ++j) {
+    uint32_t vw[4];
+    words4(t.v[j], vw);  // dims 8c .. 8c + 7 of token 4 j + r
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // (dim 2i of both tokens) and (dim 2i + 1 of both tokens) as bf16 pairs
-      const uint32_t even = (va[i] & 0xffffu) | (vb[i] << 16);
-      const uint32_t odd = (va[i] >> 16) | (vb[i] & 0xffff0000u);
+      const float ve = __uint_as_float(vw[i] << 16);
+      const float vo = __uint_as_float(vw[i] & 0xffff0000u);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        st.acc[h][2 * i] = dot2_bf16(pp[u][h], even, st.acc[h][2 * i]);
-        st.acc[h][2 * i + 1] = dot2_bf16(pp[u][h], odd, st.acc[h][2 * i + 1]);
+        st.acc[h][2 * i] = fmaf(pf[j][h], ve, st.acc[h][2 * i]);
+        st.acc[h][2 * i + 1] = fmaf(pf[j][h], vo, st.acc[h][2 * i + 1]);
       }
     }
   }
