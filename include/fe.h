@@ -419,6 +419,25 @@ int fe_kv_allocator_batch(const fe_kv_allocator* a, const int* seqs, int n, int3
                           int32_t pad_block, int32_t* context_lens);
 
 /*
+ * Measurement helper, not part of the attention path: the HBM read ceiling
+ * of the decode kernel's load form, for benchmarks to report beside the
+ * kernels' rates.  Reads the n whole 4 KiB tiles base[tile_ids[i] * 4096 ..
+ * + 4095] (i < n), each with one wave's four 1 KiB runs of non-temporal
+ * 16-byte buffer loads, 16 tiles per wave, and XOR-folds each wave's data
+ * into sink[i / 16] (sink: uint32 [ceil(n / 16)], device, overwritten).
+ *   base       device buffer of num_tiles * 4096 bytes, 16-byte aligned
+ *   tile_ids   int32 [n] device; ids outside [0, num_tiles) are skipped
+ *              (never read)
+ * Asynchronous on `stream`; n == 0 is a no-op.  Errors: FE_ERR_NULL,
+ * FE_ERR_INVALID_ARG (num_tiles <= 0, n < 0, misaligned base), FE_ERR_HIP.
+ * Source: ForgeLM README, "Tooling and Benchmarks" (performance claims need
+ * reproducible measurement) and "Documentation" ("Measured optimization over
+ * speculative abstraction").
+ */
+int fe_hbm_read_probe(const void* base, int64_t num_tiles, const int32_t* tile_ids, int n, uint32_t* sink,
+                      hipStream_t stream);
+
+/*
  * Static description of a status code (never NULL; "FE_ERR_UNKNOWN" for a
  * value that is not an fe_status).
  * Source: ForgeLM README, "Proposed Stack" (a C/C++ native backend reached

@@ -83,6 +83,8 @@ def load_library():
     lib.fe_sampler_workspace_size.restype = Z
     lib.fe_sampler_softmax_argmax.argtypes = [P, P, P, P, P, I, I, P, Z, P]
     lib.fe_sampler_softmax_argmax.restype = I
+    lib.fe_hbm_read_probe.argtypes = [P, ctypes.c_int64, P, I, P, P]
+    lib.fe_hbm_read_probe.restype = I
     lib.fe_status_string.argtypes = [I]
     lib.fe_status_string.restype = ctypes.c_char_p
     lib.fe_last_error.argtypes = []
@@ -411,6 +413,20 @@ def fe_sampler_softmax_argmax(probs, lse, argmax, logits, inv_temperature=None, 
         _dev(inv_temperature, torch.float32, "inv_temperature", 1), B, V, _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream))
     _check(rc, "fe_sampler_softmax_argmax")
+
+
+def fe_hbm_read_probe(base, tile_ids, sink, stream=None) -> None:
+    """Read the 4 KiB tiles of uint8 device buffer ``base`` listed in int32
+    ``tile_ids`` with the decode kernel's load form (a read-rate probe);
+    ``sink`` is an int32 device tensor of ceil(n / 16) words."""
+    _shape(base, "base", None)
+    _shape(tile_ids, "tile_ids", None)
+    n = tile_ids.shape[0]
+    _shape(sink, "sink", (n + 15) // 16)
+    rc = load_library().fe_hbm_read_probe(
+        _dev(base, torch.uint8, "base", 1), base.numel() // 4096, _dev(tile_ids, torch.int32, "tile_ids", 1), n,
+        _dev(sink, torch.int32, "sink", 1), _stream(stream))
+    _check(rc, "fe_hbm_read_probe")
 
 
 # ----------------------------------------------------------------------------

@@ -348,4 +348,19 @@ int fe_sampler_softmax_argmax(float* probs, float* lse, int32_t* argmax, const v
   }
 }
 
+int fe_hbm_read_probe(const void* base, int64_t num_tiles, const int32_t* tile_ids, int n, uint32_t* sink,
+                      hipStream_t stream) {
+  static const char* fn = "fe_hbm_read_probe";
+  try {
+    if (num_tiles <= 0 || n < 0) return fail(FE_ERR_INVALID_ARG, fn, "num_tiles must be positive and n >= 0");
+    if (n == 0) return FE_OK;
+    if (!base || !tile_ids || !sink) return fail(FE_ERR_NULL, fn, "base, tile_ids and sink must not be NULL");
+    if (!aligned16(base)) return fail(FE_ERR_INVALID_ARG, fn, "base must be 16-byte aligned");
+    const hipError_t e = fe::launch_hbm_read_probe(base, num_tiles, tile_ids, n, sink, stream);
+    return e == hipSuccess ? FE_OK : hip_fail(e, fn);
+  } catch (...) {
+    return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
+  }
+}
+
 }  // extern "C"

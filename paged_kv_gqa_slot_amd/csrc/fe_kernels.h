@@ -136,6 +136,12 @@ struct SamplerArgs {
   void* workspace;
 };
 
+// HBM read probe (hbm_probe.hip): each wave reads kProbeTilesPerWave tiles
+// of 4 KiB and writes one word of sink.
+constexpr int kProbeTilesPerWave = 16;
+hipError_t launch_hbm_read_probe(const void* base, int64_t num_tiles, const int32_t* tile_ids, int n, uint32_t* sink,
+                                 hipStream_t stream);
+
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_cache,
                             void* v_cache, int T, int num_blocks, int Hkv, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -493,3 +493,14 @@ def test_decode_noalloc_argument_errors(lib):
     assert "32" in fe.fe_last_error() and "scratch" in fe.fe_last_error()
     # the gate-sized call fits (64 x 32 heads x 8 partitions: ~8.5 MB)
     assert ws(64, 32, 8, 128, 8192, 0) <= (32 << 20)
+
+
+def test_hbm_read_probe_argument_errors(lib):
+    f = lib.fe_hbm_read_probe
+    assert f(P, 16, P, 0, P, None) == OK  # nothing to read
+    assert f(None, 16, P, 4, P, None) == NULL
+    assert f(P, 16, None, 4, P, None) == NULL
+    assert f(P, 16, P, 4, None, None) == NULL
+    assert f(P, 0, P, 4, P, None) == INVALID
+    assert f(P, 16, P, -1, P, None) == INVALID
+    assert f(P + 4, 16, P, 4, P, None) == INVALID
