@@ -421,11 +421,14 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<
 
   // Fused split-K merge: the last of the sequence's np partitions to arrive
   // combines all of them by log-sum-exp.  The partials travel through
-  // device-scope stores and loads (coherent across the XCDs' L2s), so no
-  // whole-cache write-back or invalidate is needed: every wave waits until
-  // its partial stores are complete (s_waitcnt vmcnt(0)) before the barrier,
-  // the arrival count is taken after it, and the last arriver reads the
-  // partials only after the count has returned.
+  // agent-scope atomic stores and loads (sc1 on gfx950: performed at the
+  // device's coherence point, past the XCDs' non-coherent L2s), so the
+  // release / acquire that orders them needs no L2 write-back or invalidate
+  // (those exist for non-atomic data): every wave waits until its partial
+  // stores are acknowledged (s_waitcnt vmcnt(0)) before the barrier, the
+  // arrival count is taken after it, and the last arriver reads the partials
+  // only after the count has returned.  An acq_rel counter adds exactly the
+  // L2 write-back / invalidate pair, which costs the mixed launch ~27%.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   if (tid == 0) {
