@@ -348,25 +348,16 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<
     consume<G, true>(st, ring[0], qw, p.scale_log2, r, rem);
   }
 
-  // merge the 4 rows of this wave: lanes c, c+16, c+32, c+48 hold the same dims
+  // merge the 4 rows of this wave: lanes c, c+16, c+32, c+48 hold the same
+  // dims (permlane swaps on the VALU, not LDS permutes)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float M = st.m[h];
-    M = fmaxf(M, __shfl_xor(M, 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
+    const float M = xor_max<32>(xor_max<16>(st.m[h]));
     const float f = fast_exp2(st.m[h] - M);
-    float l = st.l[h] * f;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    st.l[h] = xor_sum<32>(xor_sum<16>(st.l[h] * f));
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float a = st.acc[h][k] * f;
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      st.acc[h][k] = a;
-    }
+    for (int k = 0; k < 8; ++k) st.acc[h][k] = xor_sum<32>(xor_sum<16>(st.acc[h][k] * f));
     st.m[h] = M;
-    st.l[h] = l;
   }
   if (r == 0) {
 #pragma unroll

@@ -61,4 +61,32 @@ __device__ __forceinline__ float sum8(float x) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// x combined with the x of lane ^ 16 (K = 16) or lane ^ 32 (K = 32), on the
+// VALU with gfx950's permlane swaps instead of an LDS permute.  A swap of x
+// with itself leaves x in one half of the result and the partner's x in the
+// other (which half depends on the lane's row), so op(half0, half1) is
+// op(x, partner) in every lane.
+template <int K>
+__device__ __forceinline__ uint2 xor_pair(float x) {
+  static_assert(K == 16 || K == 32, "permlane swaps exchange rows 16 or 32 lanes apart");
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (K == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return make_uint2(s[0], s[1]);
+  } else {
+    const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return make_uint2(s[0], s[1]);
+  }
+}
+template <int K>
+__device__ __forceinline__ float xor_sum(float x) {
+  const uint2 p = xor_pair<K>(x);
+  return __uint_as_float(p.x) + __uint_as_float(p.y);
+}
+template <int K>
+__device__ __forceinline__ float xor_max(float x) {
+  const uint2 p = xor_pair<K>(x);
+  return fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+}
+
 }  // namespace fe
