@@ -78,6 +78,16 @@ __device__ __forceinline__ uint2 xor_pair(float x) {
     return make_uint2(s[0], s[1]);
   }
 }
+// The x of lane ^ K (K = 16 or 32): the half of the swap that is not this
+// lane's own, which is the second half in rows 0 and 2 (K = 16) or in rows 0
+// and 1 (K = 32).
+template <int K>
+__device__ __forceinline__ float xor_partner(float x) {
+  const uint2 p = xor_pair<K>(x);
+  const int lane = __lane_id();
+  const bool own_first = K == 16 ? ((lane >> 4) & 1) == 0 : (lane >> 5) == 0;
+  return __uint_as_float(own_first ? p.y : p.x);
+}
 template <int K>
 __device__ __forceinline__ float xor_sum(float x) {
   const uint2 p = xor_pair<K>(x);

@@ -55,6 +55,39 @@ __device__ __forceinline__ void merge_best(float& v, int& i, float v2, int i2) {
   }
 }
 
+// Exchange (m, sum, best value, best index) with one partner lane and merge:
+// kCtrl is a DPP control within 16-lane rows, or 16 / 32 for the permlane
+// swaps across rows.  Both lanes of a pair compute the same merge (both
+// merges are symmetric), so after quad xor 1, quad xor 2, the half-row and
+// row mirrors and the two swaps every lane holds the wave's result.
+template <int kCtrl>
+__device__ __forceinline__ void exchange(float& m, float& sum, float& best_v, int& best_i) {
+  float m2, sum2, v2;
+  int i2;
+  if constexpr (kCtrl == 16 || kCtrl == 32) {
+    m2 = xor_partner<kCtrl>(m);
+    sum2 = xor_partner<kCtrl>(sum);
+    v2 = xor_partner<kCtrl>(best_v);
+    i2 = __float_as_int(xor_partner<kCtrl>(__int_as_float(best_i)));
+  } else {
+    m2 = dpp<kCtrl>(m);
+    sum2 = dpp<kCtrl>(sum);
+    v2 = dpp<kCtrl>(best_v);
+    i2 = __float_as_int(dpp<kCtrl>(__int_as_float(best_i)));
+  }
+  merge_ms(m, sum, m2, sum2);
+  merge_best(best_v, best_i, v2, i2);
+}
+
+__device__ __forceinline__ void wave_merge(float& m, float& sum, float& best_v, int& best_i) {
+  exchange<kDppQuadXor1>(m, sum, best_v, best_i);
+  exchange<kDppQuadXor2>(m, sum, best_v, best_i);
+  exchange<kDppRowHalfMirror>(m, sum, best_v, best_i);
+  exchange<kDppRowMirror>(m, sum, best_v, best_i);
+  exchange<16>(m, sum, best_v, best_i);
+  exchange<32>(m, sum, best_v, best_i);
+}
+
 __device__ __forceinline__ float row_scale(const SamplerParams& p, int b) {
   return (p.inv_temp ? p.inv_temp[b] : 1.0f) * kLog2e;
 }
@@ -102,11 +135,7 @@ __global__ __launch_bounds__(kThreads) void sampler_partial_kernel(SamplerParams
     sum = t;
   }
   // wave, then workgroup
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    merge_ms(m, sum, __shfl_xor(m, off), __shfl_xor(sum, off));
-    merge_best(best_v, best_i, __shfl_xor(best_v, off), __shfl_xor(best_i, off));
-  }
+  wave_merge(m, sum, best_v, best_i);
   __shared__ Partial sh[kWaves];
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) sh[wave] = Partial{m, sum, best_v, best_i};
@@ -139,11 +168,7 @@ __device__ __forceinline__ RowTotals merge_row(const SamplerParams& p, int b, in
     merge_ms(M, Z, q.m, q.sum);
     merge_best(best_v, best_i, q.best_v, q.best_i);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    merge_ms(M, Z, __shfl_xor(M, off), __shfl_xor(Z, off));
-    merge_best(best_v, best_i, __shfl_xor(best_v, off), __shfl_xor(best_i, off));
-  }
+  wave_merge(M, Z, best_v, best_i);
   const bool empty = M == -INFINITY;
   if (c == 0 && threadIdx.x == 0) {
     p.argmax[b] = empty ? 0 : best_i;
