@@ -299,3 +299,32 @@ def test_decode_append_random_shapes(dev):
         parts = (0, 1, int(torch.randint(2, 10, (1,), generator=g)))
         w = inputs.custom("decode", B, G * Hkv, Hkv, lens, 700 + case, append=1, poison="nan")
         run_decode_append(w, dev, parts=parts, label=f"fused random #{case} G={G} Hkv={Hkv} lens={lens}")
+
+
+# -- decode: sizes at the edges of the plan ----------------------------------------
+
+def test_decode_one_very_long_sequence(dev):
+    """One sequence of 131072 tokens (8192 blocks): the automatic plan (64
+    partitions of 128 blocks), 40 partitions, and a request for 16 that the
+    256-block limit of a partition raises to 32; the merge walks the partials
+    in chunks of 16."""
+    w = inputs.custom("decode", 1, 32, 8, [131072], 901, append=1, poison="nan")
+    assert fe.fe_paged_gqa_decode_num_partitions(1, 32, 8, 128, w.max_context_len, 16) == 32
+    run_decode(w, dev, parts=(0, 40, 16), label="1 x 131072")
+
+
+def test_decode_many_partitions(dev):
+    """Partition counts far above the automatic choice, down to one block per
+    partition (the merge then combines up to 129 partials per row)."""
+    lens = [2049, 17, 1000, 0, 512]
+    w = inputs.custom("decode", len(lens), 16, 4, lens, 902, append=1, poison="nan")
+    run_decode(w, dev, parts=(50, 100, 129, 1000), label="many partitions")
+
+
+def test_decode_many_sequences(dev):
+    """1024 sequences of short ragged contexts (0..300 tokens): a grid of
+    tens of thousands of workgroups, single pass and split."""
+    g = torch.Generator().manual_seed(903)
+    lens = torch.randint(0, 301, (1024,), generator=g).tolist()
+    w = inputs.custom("decode", 1024, 16, 8, lens, 903, append=1, poison="large")
+    run_decode(w, dev, parts=(1, 0, 3), label="1024 sequences")
