@@ -51,11 +51,8 @@ namespace pre {
 
 constexpr int kKeysPerTile = 64;
 constexpr int kRowBytes = kHeadDim * 2;                 // 256 bytes of one K/V row
-constexpr int kKStride = kRowBytes + 16;                // padded LDS row strides
-constexpr int kVStride = kRowBytes + 64;
-constexpr int kKTileBytes = kKeysPerTile * kKStride;    // 17408
-constexpr int kVTileBytes = kKeysPerTile * kVStride;    // 20480
-constexpr int kBufBytes = kKTileBytes + kVTileBytes;    // one K + V tile
+constexpr int kTileBytes = kKeysPerTile * kRowBytes;    // one K or V tile in LDS: 16 KiB, rows unpadded
+constexpr int kGroupBytes = 4 * kTileBytes;             // a key group's two K and two V tiles
 constexpr float kRescaleSlack = 8.0f;
 constexpr float kEmptyMax = -1.0e30f;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -88,10 +85,47 @@ struct Shape {
   static constexpr int kThreads = 64 * W * KS;
   // a 64-key tile is 4 KV blocks; wave w of a group stages blocks w, w + W, ...
   static constexpr int kStageBlocks = (4 + W - 1) / W;
-  static constexpr int kLdsBytes = 2 * KS * kBufBytes;
+  static constexpr int kLdsBytes = KS * kGroupBytes;
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// One 4 KiB (block, KV head) tile straight from global memory into LDS:
+// four buffer loads with the LDS bit, each writing 64 lanes x 16 bytes
+// contiguously at LDS byte address m0 + 1024 j (the instruction offset moves
+// the global address by the same 1024 j).  Lane i's voffset v_j picks which
+// 16 bytes of its 256-byte row it fetches, which is how the LDS rows get
+// their XOR swizzle.  Bytes at or past `bytes` read as zeros without a memory
+// access.  Written as asm because the compiler's builtin makes every later
+// LDS read wait for all such loads in flight; the caller waits for them with
+// s_waitcnt vmcnt (the loads count there, completing in issue order).  M0 is
+// saved and restored around the loads, with the wait state that an M0 write
+// before an LDS-direct load needs.
+__device__ __forceinline__ void lds_direct_tile(const uint16_t* base, int bytes, uint32_t m0, uint32_t v0,
+                                                uint32_t v1, uint32_t v2, uint32_t v3) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0), bytes, 0x00020000);
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %[save], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[v0], %[r], 0 offen offset:0 lds\n\t"
+      "buffer_load_dwordx4 %[v1], %[r], 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %[v2], %[r], 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %[v3], %[r], 0 offen offset:3072 lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %[save]"
+      : [save] "=&s"(save)
+      : [m0] "s"(m0), [r] "s"(r), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [v3] "v"(v3)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Query tile qt of sequence b against KV head g, run by the whole workgroup
 // (Shape<G, KSel>::kThreads threads); lds holds Shape<G, KSel>::kLdsBytes bytes.
@@ -153,17 +187,20 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   const size_t blk_stride = static_cast<size_t>(p.Hkv) * kTileElems;
   const uint16_t* kg = p.k_cache + static_cast<size_t>(g) * kTileElems;
   const uint16_t* vg = p.v_cache + static_cast<size_t>(g) * kTileElems;
-  const int grp_base = grp * 2 * kBufBytes;
+  const int grp_base = grp * kGroupBytes;  // this group's K tiles 0, 1, then V tiles 0, 1
+  const int n_g = t_end - t_first;         // this group's tiles
 
   // Staging: wave w copies blocks w, w + W, ... of each 64-key tile, each a
-  // contiguous 4 KiB (block, KV head) run, lane reading 16 bytes at
-  // lane + 64 j (token row 4 j + lane / 16, chunk lane % 16).  Rows past the
-  // context come back as zeros from the buffer range (never NaN, so masked
-  // keys stay inert in the PV product).
+  // contiguous 4 KiB (block, KV head) run, straight into LDS (no registers).
+  // Rows past the context come back as zeros from the buffer range (never
+  // NaN, so masked keys stay inert in the PV product).  LDS rows are 256
+  // bytes, unpadded; their 16-byte chunks are XOR-swizzled so that both read
+  // patterns below are free of bank conflicts on the 64 banks:
+  //   K row r holds logical chunk c at chunk c ^ (r & 15)  (16 rows read at
+  //     one chunk hit 16 different chunks),
+  //   V row r holds logical chunk c at chunk c ^ 4 (r & 3)  (the transposed
+  //     reads of 4 rows x 64 bytes hit 4 different 64-byte groups).
   const int nblk_seq = (L + kBlockSize - 1) / kBlockSize;
-  const int st_k = grp_base + (lane >> 4) * kKStride + (lane & 15) * 16;
-  const int st_v = grp_base + kKTileBytes + (lane >> 4) * kVStride + (lane & 15) * 16;
-  uint4 rk[S::kStageBlocks][4], rv[S::kStageBlocks][4];
   // Block ids of the blocks this wave stages, held in VGPRs so a fetch needs
   // no dependent scalar load: lane j of ids[i] holds the (clamped) id of
   // block wave + i W of local tile 64 chunk + j, or 0 past the context.
@@ -176,63 +213,86 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
       const int lt = 64 * chunk + lane;
       const int gb = 4 * (t_first + lt) + bl;
       int v = 0;
-      if (bl < 4 && lt < t_end - t_first && gb < nblk_seq) v = min(max(bt[gb], 0), p.num_blocks - 1);
+      if (bl < 4 && lt < n_g && gb < nblk_seq) v = min(max(bt[gb], 0), p.num_blocks - 1);
       ids[i] = v;
     }
     ids_chunk = chunk;
   };
-  auto fetch = [&](int t) __attribute__((always_inline)) {
+  // blocks this wave stages per tile, and the LDS-direct loads that makes
+  int n_stage = 0;
+#pragma unroll
+  for (int i = 0; i < S::kStageBlocks; ++i) n_stage += wave + i * S::W < 4 ? 1 : 0;
+  // Global byte offsets of this lane's 16 bytes within the j-th 1 KiB run
+  // (rows 4 j .. 4 j + 3 of a block; the 1024 j itself is the instruction
+  // offset), for the swizzles above: a block's rows are rows 16 bl + r of
+  // the tile, and 16 bl changes neither r & 15 nor r & 3.
+  uint32_t kvo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kvo[j] = (lane >> 4) * kRowBytes + (((lane & 15) ^ ((4 * j + (lane >> 4)) & 15)) << 4);
+  const uint32_t vvo = (lane >> 4) * kRowBytes + (((lane & 15) ^ (4 * (lane >> 4))) << 4);
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) + grp_base;
+  // where tile t's blocks come from (offset into the pools, valid bytes);
+  // the V copy of a tile runs one phase after its K copy and reuses these
+  size_t src_off[S::kStageBlocks];
+  int src_bytes[S::kStageBlocks];
+  auto locate = [&](int t) __attribute__((always_inline)) {
     const int lt = t - t_first;
-    if ((lt >> 6) != ids_chunk) load_ids(lt >> 6);
+    if (lt < n_g && (lt >> 6) != ids_chunk) {
+      load_ids(lt >> 6);
+      wait_vm<0>();
+    }
 #pragma unroll
     for (int i = 0; i < S::kStageBlocks; ++i) {
       const int bl = wave + i * S::W;
-      if (bl < 4) {
-        const int gb = 4 * t + bl;  // block index within the sequence
-        const bool ok = gb < nblk_seq;
-        const int blk = __builtin_amdgcn_readlane(ids[i], lt & 63);
-        const int rows = ok ? min(kBlockSize, L - gb * kBlockSize) : 0;
-        const size_t o = static_cast<size_t>(blk) * blk_stride;
-        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(kg + o), static_cast<short>(0), rows * kRowBytes, 0x00020000);
-        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(vg + o), static_cast<short>(0), rows * kRowBytes, 0x00020000);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kr, lane * 16 + 1024 * j, 0, 0);
-          const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(vr, lane * 16 + 1024 * j, 0, 0);
-          rk[i][j] = make_uint4(a[0], a[1], a[2], a[3]);
-          rv[i][j] = make_uint4(c[0], c[1], c[2], c[3]);
-        }
-      }
+      const int gb = 4 * t + bl;  // block index within the sequence
+      const bool ok = lt < n_g && gb < nblk_seq;
+      src_off[i] = static_cast<size_t>(__builtin_amdgcn_readlane(ids[i], lt & 63)) * blk_stride;
+      src_bytes[i] = ok ? min(kBlockSize, L - gb * kBlockSize) * kRowBytes : 0;
     }
   };
-  // the staged tile goes to LDS buffer `buf` (tile j of the group: buffer j % 2)
-  auto stash = [&](auto bufc) __attribute__((always_inline)) {
-    constexpr int buf = decltype(bufc)::value;
+  // K of tile t into K buffer kb, from the locations just looked up
+  auto stage_k = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < S::kStageBlocks; ++i) {
       const int bl = wave + i * S::W;
-      if (bl < 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = 16 * bl + 4 * j;
-          *reinterpret_cast<uint4*>(&lds[st_k + buf * kBufBytes + row * kKStride]) = rk[i][j];
-          *reinterpret_cast<uint4*>(&lds[st_v + buf * kBufBytes + row * kVStride]) = rv[i][j];
-        }
-      }
+      if (bl < 4)
+        lds_direct_tile(kg + src_off[i], src_bytes[i], lds_addr + kb * kTileBytes + bl * 4096, kvo[0], kvo[1],
+                        kvo[2], kvo[3]);
     }
+  };
+  // V of the tile located by the previous locate() into V buffer vb
+  auto stage_v = [&](int vb, const size_t (&off)[S::kStageBlocks], const int (&bytes)[S::kStageBlocks])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < S::kStageBlocks; ++i) {
+      const int bl = wave + i * S::W;
+      if (bl < 4)
+        lds_direct_tile(vg + off[i], bytes[i], lds_addr + (2 + vb) * kTileBytes + bl * 4096, vvo, vvo, vvo, vvo);
+    }
+  };
+  // every copy this wave issued before its latest 2 n_stage tiles has landed
+  auto wait_previous = [&]() __attribute__((always_inline)) {
+    if (n_stage == 1) wait_vm<8>();
+    else if (n_stage == 2) wait_vm<16>();
   };
 
-  // per-lane LDS read bases; everything else is a compile-time offset
-  // K rows for S^T: key 32 blk + col, dims 16 kk + 8 half
-  const int k_rd = grp_base + col * kKStride + half * 16;
+  // per-lane LDS read addresses (the buffer, key block and tau parts are
+  // compile-time offsets)
+  // K rows for S^T: key 32 blk + col, logical chunk 2 kk + half
+  int kra[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kra[kk] = grp_base + col * kRowBytes + (((2 * kk + half) ^ (col & 15)) << 4);
   // transposed V reads: k-slots of step (blk, tau) are keys 32 blk + 16 tau +
   // {0-3, 8-11, 4-7, 12-15}; 16-lane group gq holds slots 8 (gq / 2) .. + 7 of
   // dims 16 (gq % 2) .. + 15 of each 32-dim block d; source lane src points at
-  // row key0 + src / 4, dims + 4 (src % 4)
+  // row key0 + src / 4 (so row & 3 = src / 4), dims + 4 (src % 4): logical
+  // chunk 2 (gq % 2) + (src % 4) / 2 + 4 d, byte 8 (src % 2) within it
   const int gq = lane >> 4, src = lane & 15;
-  const int v_rd = grp_base + kKTileBytes + (4 * (gq >> 1) + (src >> 2)) * kVStride + 32 * (gq & 1) + 8 * (src & 3);
+  int vra[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    vra[d] = grp_base + 2 * kTileBytes + (4 * (gq >> 1) + (src >> 2)) * kRowBytes +
+             ((2 * (gq & 1) + ((src & 3) >> 1) + 4 * (d ^ (src >> 2))) << 4) + 8 * (src & 1);
 
   f32x16_t o_acc[4];  // O^T, dim block d: lane holds query col, dims 32 d + 8 (i / 4) + 4 half + i % 4
 #pragma unroll
@@ -257,7 +317,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(&lds[k_rd + buf * kBufBytes + blk * 32 * kKStride + kk * 32]);
+        const uint4 kv = *reinterpret_cast<const uint4*>(&lds[kra[kk] + buf * kTileBytes + blk * 32 * kRowBytes]);
         acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qb[kk], acc[blk], 0, 0, 0);
       }
     s[0] = acc[0];
@@ -273,11 +333,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
       for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const int o = v_rd + buf * kBufBytes + (32 * blk + 16 * tau) * kVStride + 64 * d;
+          const int o = vra[d] + buf * kTileBytes + (32 * blk + 16 * tau) * kRowBytes;
           const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) s16x4_t*)(&lds[o]));
           const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(&lds[o + 8 * kVStride]));
+              (__attribute__((address_space(3))) s16x4_t*)(&lds[o + 8 * kRowBytes]));
           // move whole dwords: element-wise 16-bit extraction here is lowered
           // into half-word shuffles that drop the upper dword of each read
           const uint2 l2 = __builtin_bit_cast(uint2, lo);
@@ -341,14 +401,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  const int n_g = t_end - t_first;  // this group's tiles
 
-  // MFMA phase of local tile i (LDS buffer bufc): S^T of tile i and, when
-  // pvc, O^T += V^T P^T of tile i - 1 (the other buffer).  One basic block;
-  // the scheduling groups keep four MFMA operands in flight from LDS so the
-  // read latency hides behind the MFMAs (16 K reads of 16 bytes for S^T, then
-  // two 8-byte transposed V reads per PV MFMA).  Measured on the 4 x (4096 +
-  // 256) chunk: 2-4 reads ahead 89-91 us, 5-6 ahead 92-93 us.
+  // MFMA phase of local tile i (K buffer bufc): S^T of tile i and, when pvc,
+  // O^T += V^T P^T of tile i - 1 (V buffer 1 - bufc).  One basic block; the
+  // scheduling groups keep four MFMA operands in flight from LDS so the read
+  // latency hides behind the MFMAs (16 K reads of 16 bytes for S^T, then two
+  // 8-byte transposed V reads per PV MFMA).
   auto mphase = [&](auto bufc, auto pvc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     using Other = std::integral_constant<int, 1 - buf>;
@@ -371,36 +429,54 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     }
   };
 
-  // One local tile i (LDS buffer i % 2 == bufc): MFMA phase, barrier,
-  // VALU/memory phase, barrier.  The O rescale in the softmax sees O with
-  // tile i - 1 already accumulated, as the online softmax requires.
+  // One local tile i (K buffer i % 2 == bufc, V buffer of tile i - 1 the
+  // other): MFMA phase, barrier, then the VALU/memory phase: V of tile i + 1
+  // into the V buffer the MFMA phase just finished reading (tile i - 1's),
+  // K of tile i + 2 into the K buffer it just finished reading (tile i's),
+  // the softmax of tile i, and a wait for the previous phase's copies (K of
+  // tile i + 1, V of tile i), which the next MFMA phase reads after the
+  // barrier.  A copy thus has a phase and a half to land.  The O rescale in
+  // the softmax sees O with tile i - 1 already accumulated, as the online
+  // softmax requires.
+  size_t v_off[S::kStageBlocks];
+  int v_bytes[S::kStageBlocks];
   auto step = [&](auto bufc, auto pvc, int i) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    using Other = std::integral_constant<int, 1 - buf>;
     mphase(bufc, pvc);
     __syncthreads();
-    // tile i + 1 (loaded during the previous phases) goes to buffer `Other`,
-    // last read by this MFMA phase's PV, which every wave finished before the
-    // barrier above; then the staging registers take tile i + 2's loads
-    if (i + 1 < n_g) stash(Other{});
-    if (i + 2 < n_g) fetch(t_first + i + 2);
+    stage_v(1 - buf, v_off, v_bytes);  // tile i + 1 (located with its K copy)
+    locate(t_first + i + 2);
+#pragma unroll
+    for (int k = 0; k < S::kStageBlocks; ++k) {
+      v_off[k] = src_off[k];
+      v_bytes[k] = src_bytes[k];
+    }
+    stage_k(buf);  // tile i + 2
     softmax(t_first + i);
+    wait_previous();
     __syncthreads();
   };
 
   // Prologue.  Q and the block ids of the first 64 tiles arrive in one
   // memory round trip, settled on every path here so that no later barrier
-  // waits on memory; each key group then stages its first tile and issues
-  // the second tile's loads before the barriers, so the two groups' first
-  // HBM round trips overlap.  Group 1 then takes one extra barrier, which
-  // puts it one phase behind group 0.
+  // waits on memory.  Each key group then copies K of its tiles 0 and 1 and V
+  // of tile 0 and waits for K of tile 0 before the barriers, so the two
+  // groups' first round trips overlap.  Group 1 then takes one extra barrier,
+  // which puts it one phase behind group 0.  Copies of tiles past a group's
+  // range read nothing and write zeros into a buffer nobody reads.
   load_ids(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (n_g > 0) {
-    fetch(t_first);
-    stash(B0{});
+  wait_vm<0>();
+  locate(t_first);
+  stage_k(0);
+  stage_v(0, src_off, src_bytes);
+  locate(t_first + 1);
+#pragma unroll
+  for (int k = 0; k < S::kStageBlocks; ++k) {
+    v_off[k] = src_off[k];
+    v_bytes[k] = src_bytes[k];
   }
-  if (n_g > 1) fetch(t_first + 1);
+  stage_k(1);
+  wait_previous();
   if (S::KS == 2 && grp == 1) __syncthreads();
   __syncthreads();
   if (n_g > 0) step(B0{}, std::false_type{}, 0);  // the first tile has no PV of a previous one
@@ -417,6 +493,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     else
       pv(B0{});
   }
+  // the copies past the range land before LDS is reused below
+  wait_vm<0>();
   if (S::KS == 2 && grp == 0) __syncthreads();
   // equal barrier counts: group 1 may have one tile fewer than group 0
   for (int k = 2 * n_g; k < 2 * nA; ++k) __syncthreads();
