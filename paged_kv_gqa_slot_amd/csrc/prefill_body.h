@@ -54,6 +54,7 @@ constexpr int kRowBytes = kHeadDim * 2;                 // 256 bytes of one K/V 
 constexpr int kTileBytes = kKeysPerTile * kRowBytes;    // one K or V tile in LDS: 16 KiB, rows unpadded
 constexpr int kGroupBytes = 4 * kTileBytes;             // a key group's two K and two V tiles
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kLazyLimit = 65536.0f;  // a lane's tile sum that makes the softmax look for a new max
 constexpr float kEmptyMax = -1.0e30f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -348,9 +349,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
       }
   };
 
-  // causal mask, running max and P = 2^(S sc - m) for absolute tile t
+  // causal mask and P = 2^(S sc - m) for absolute tile t.  The running max
+  // m is raised lazily: the weights are first taken against the current m;
+  // only when some lane's sum over the tile leaves [0, kLazyLimit] (the first
+  // tile, with m still at kEmptyMax, always does) is the tile's true max
+  // taken, m raised where it grew by more than kRescaleSlack, and the weights
+  // taken again.  Between raises a weight can reach about kLazyLimit, far
+  // inside fp32 and bf16 range; the max search costs nothing on the tiles
+  // that do not raise it.
   auto softmax = [&](int t) __attribute__((always_inline)) {
-    float mx = -INFINITY;
     if (t >= n_plain) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -360,16 +367,37 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
           if (key > pos || !q_valid) s[blk][i2] = -INFINITY;
         }
     }
+    auto weights = [&]() __attribute__((always_inline)) {
+      float ts = 0.f;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, s[blk][i2]);
-    mx *= sc;
-    {
+        for (int tau = 0; tau < 2; ++tau) {
+          float e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            e[j] = fast_exp2(fmaf(s[blk][8 * tau + j], sc, -m));
+            ts += e[j];
+          }
+          uint4 w;
+          w.x = pack_bf16x2(e[0], e[1]);
+          w.y = pack_bf16x2(e[2], e[3]);
+          w.z = pack_bf16x2(e[4], e[5]);
+          w.w = pack_bf16x2(e[6], e[7]);
+          pb[blk][tau] = as_bf16x8(w);
+        }
+      return ts;
+    };
+    float ts = weights();
+    if (__any(!(ts <= kLazyLimit))) {  // also true for inf / NaN
+      float mx = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, s[blk][i2]);
+      mx *= sc;
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    if (__any(mx > m + kRescaleSlack)) {
       if (mx > m + kRescaleSlack) {
         const float a = fast_exp2(m - mx);
         m = mx;
@@ -379,24 +407,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
 #pragma unroll
           for (int i2 = 0; i2 < 16; ++i2) o_acc[d][i2] *= a;
       }
+      ts = weights();
     }
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          e[j] = fast_exp2(fmaf(s[blk][8 * tau + j], sc, -m));
-          lsum += e[j];
-        }
-        uint4 w;
-        w.x = pack_bf16x2(e[0], e[1]);
-        w.y = pack_bf16x2(e[2], e[3]);
-        w.z = pack_bf16x2(e[4], e[5]);
-        w.w = pack_bf16x2(e[6], e[7]);
-        pb[blk][tau] = as_bf16x8(w);
-      }
+    lsum += ts;
   };
 
   using B0 = std::integral_constant<int, 0>;
@@ -442,7 +455,13 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   int v_bytes[S::kStageBlocks];
   auto step = [&](auto bufc, auto pvc, int i) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
+    // the MFMA phase runs at the highest wave priority: on each SIMD its
+    // MFMAs and operand reads then go first, and the other group's softmax
+    // fills the issue cycles between them (the second-created wave of a SIMD
+    // otherwise lost the arbitration in both phases)
+    __builtin_amdgcn_s_setprio(3);
     mphase(bufc, pvc);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     stage_v(1 - buf, v_off, v_bytes);  // tile i + 1 (located with its K copy)
     locate(t_first + i + 2);
