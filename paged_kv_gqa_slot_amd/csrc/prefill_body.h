@@ -368,17 +368,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
         }
     }
     auto weights = [&]() __attribute__((always_inline)) {
-      float ts = 0.f;
+      float part[4];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
           float e[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            e[j] = fast_exp2(fmaf(s[blk][8 * tau + j], sc, -m));
-            ts += e[j];
-          }
+          for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(s[blk][8 * tau + j], sc, -m));
+          // pairwise sums: short dependency chains in the critical VALU phase
+          part[2 * blk + tau] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
           uint4 w;
           w.x = pack_bf16x2(e[0], e[1]);
           w.y = pack_bf16x2(e[2], e[3]);
@@ -386,7 +385,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
           w.w = pack_bf16x2(e[6], e[7]);
           pb[blk][tau] = as_bf16x8(w);
         }
-      return ts;
+      return (part[0] + part[1]) + (part[2] + part[3]);
     };
     float ts = weights();
     if (__any(!(ts <= kLazyLimit))) {  // also true for inf / NaN
