@@ -80,3 +80,43 @@ def test_sampler_no_temperature_and_no_probs(dev):
 def test_sampler_qwen3_vocab_batch64(dev):
     """The sampler step of the 64-sequence decode batch over the full Qwen3 vocabulary."""
     run(inputs.sampler_case(64, inputs.QWEN3_VOCAB, seed=5), dev, "Qwen3 vocab B=64")
+
+
+def test_sampler_workspace_reused(dev):
+    """One workspace of the largest size serves calls of different shapes in
+    turn (each call's partials overwrite the previous call's)."""
+    V = inputs.QWEN3_VOCAB
+    ws = torch.empty(fe.fe_sampler_workspace_size(256, V), dtype=torch.uint8, device=dev)
+    for B, seed in [(64, 21), (8, 22), (256, 23), (64, 24)]:
+        c = inputs.sampler_case(B, V, seed=seed)
+        x, it = c.logits.to(dev), c.inv_temperature.to(dev)
+        probs = torch.empty((B, V), dtype=torch.float32, device=dev)
+        lse = torch.empty((B,), dtype=torch.float32, device=dev)
+        am = torch.empty((B,), dtype=torch.int32, device=dev)
+        fe.fe_sampler_softmax_argmax(probs, lse, am, x, it, workspace=ws)
+        torch.cuda.synchronize()
+        rows = sorted({0, B // 3, B - 1})
+        rp, rl, ra = oracle.sampler(c.logits[rows], c.inv_temperature[rows])
+        assert np.array_equal(am.cpu().numpy()[rows], ra), (B, "argmax")
+        assert float(np.abs(lse.cpu().numpy()[rows].astype(np.float64) - rl).max()) <= LSE_ABS, (B, "lse")
+        gp = probs.cpu().numpy()[rows].astype(np.float64)
+        assert (np.abs(gp - rp) <= REL * rp + ABS).all(), (B, "probs")
+
+
+def test_sampler_more_rows_than_resident_workgroups(dev):
+    """1024 rows of the full vocabulary: ten ranges per row and ten times more
+    workgroups than the GPU holds at once.  Sampled rows against the oracle."""
+    B, V = 1024, inputs.QWEN3_VOCAB
+    c = inputs.sampler_case(B, V, seed=31)
+    x, it = c.logits.to(dev), c.inv_temperature.to(dev)
+    probs = torch.empty((B, V), dtype=torch.float32, device=dev)
+    lse = torch.empty((B,), dtype=torch.float32, device=dev)
+    am = torch.empty((B,), dtype=torch.int32, device=dev)
+    fe.fe_sampler_softmax_argmax(probs, lse, am, x, it)
+    torch.cuda.synchronize()
+    rows = list(range(0, B, 97)) + [B - 1]
+    rp, rl, ra = oracle.sampler(c.logits[rows], c.inv_temperature[rows])
+    assert np.array_equal(am.cpu().numpy()[rows], ra), "argmax"
+    assert float(np.abs(lse.cpu().numpy()[rows].astype(np.float64) - rl).max()) <= LSE_ABS, "lse"
+    gp = probs.cpu().numpy()[rows].astype(np.float64)
+    assert (np.abs(gp - rp) <= REL * rp + ABS).all(), "probs"
