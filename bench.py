@@ -78,6 +78,33 @@ def streaming_read_ceiling(torch, dev, fe):
                       "same run (sequential order beside it)"}
 
 
+def sustained_mfma_ceiling(torch, dev, fe):
+    """Same-run bf16 MFMA rate of the prefill tile's instruction
+    (fe_mfma_rate_probe: v_mfma_f32_32x32x16_bf16 back to back, two waves per
+    SIMD, every CU busy, operands of seeded random data) over about a
+    millisecond.  A secondary reference beside the 2.5 PFLOP/s peak: the
+    published figure assumes a clock the chip does not hold with every CU
+    issuing MFMAs."""
+    g = torch.Generator(device="cpu").manual_seed(54321)
+    ops = torch.rand(1 << 16, generator=g).to(torch.bfloat16).to(dev)  # 8192 16-byte operands
+    wgs, rounds = 1024, 256  # 4 workgroups per CU
+    sink = torch.empty(wgs * 8, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        fe.fe_mfma_rate_probe(ops, wgs, rounds, sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(5):
+        fe.fe_mfma_rate_probe(ops, wgs, rounds, sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    flops = wgs * 8 * rounds * 64 * 32768
+    return {"TFLOPs": round(flops / (a.elapsed_time(b) / 5 * 1e-3) / 1e12, 1),
+            "method": "fe_mfma_rate_probe: v_mfma_f32_32x32x16_bf16 on random bf16 operands, 2 waves per SIMD on "
+                      "every CU, same run"}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -663,6 +690,9 @@ def main():
                 "kernel": "fe_paged_gqa_prefill_chunk (gqa_prefill_chunk_kernel)", "per_launch_flops": flops,
                 "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5), **att_spread,
                 "cold_median_ms": round(cold_med_ms, 5)}
+        mceil = sustained_mfma_ceiling(torch, dev, fe)
+        roof["sustained_mfma_ceiling"] = mceil
+        roof["frac_of_sustained_mfma_ceiling"] = round(achieved / mceil["TFLOPs"], 4)
         metric = "paged GQA chunked-prefill TFLOP/s (% of bf16 MFMA peak), Qwen3-4B shape"
         unit = "TFLOP/s"
         extra = {}

@@ -438,6 +438,28 @@ int fe_hbm_read_probe(const void* base, int64_t num_tiles, const int32_t* tile_i
                       hipStream_t stream);
 
 /*
+ * Measurement helper, not part of the attention path: the bf16 MFMA rate the
+ * device sustains with the prefill tile's instruction
+ * (v_mfma_f32_32x32x16_bf16, 32 x 32 x 16, 32768 flop each).  Launches
+ * `workgroups` workgroups of 8 waves (two per SIMD, as the prefill tile
+ * runs); wave i loads 8 A and 8 B operands per lane from `operands`
+ * (16-byte entries ((i * 16 + k) * 64 + lane) mod n_ops, k < 16), then issues
+ * rounds * 64 MFMAs on 8 independent accumulators (round r, step j pairs
+ * accumulator k with A[(j + k) mod 8] and B[k]) and writes the sum of its
+ * accumulators to sink[i].  Flops of a call:
+ * workgroups * 8 * rounds * 64 * 32768.
+ *   operands    device, n_ops 16-byte entries of bf16 pairs, 16-byte aligned
+ *   sink        fp32 [workgroups * 8], device, overwritten
+ * Asynchronous on `stream`; workgroups == 0 is a no-op.  Errors: FE_ERR_NULL,
+ * FE_ERR_INVALID_ARG (n_ops <= 0, workgroups or rounds < 0, misaligned
+ * operands), FE_ERR_UNSUPPORTED (a grid of 2^31 threads or more), FE_ERR_HIP.
+ * Source: ForgeLM README, "Tooling and Benchmarks" (performance claims need
+ * reproducible measurement) and "Documentation" ("Measured optimization over
+ * speculative abstraction").
+ */
+int fe_mfma_rate_probe(const void* operands, int n_ops, int workgroups, int rounds, float* sink, hipStream_t stream);
+
+/*
  * Static description of a status code (never NULL; "FE_ERR_UNKNOWN" for a
  * value that is not an fe_status).
  * Source: ForgeLM README, "Proposed Stack" (a C/C++ native backend reached

@@ -8,6 +8,7 @@ library is an error -- there is no CPU fallback.
 from .binding import (  # noqa: F401
     KVAllocator,
     fe_hbm_read_probe,
+    fe_mfma_rate_probe,
     fe_kv_allocator_append,
     fe_kv_allocator_batch,
     fe_kv_allocator_create,

@@ -85,6 +85,8 @@ def load_library():
     lib.fe_sampler_softmax_argmax.restype = I
     lib.fe_hbm_read_probe.argtypes = [P, ctypes.c_int64, P, I, P, P]
     lib.fe_hbm_read_probe.restype = I
+    lib.fe_mfma_rate_probe.argtypes = [P, I, I, I, P, P]
+    lib.fe_mfma_rate_probe.restype = I
     lib.fe_status_string.argtypes = [I]
     lib.fe_status_string.restype = ctypes.c_char_p
     lib.fe_last_error.argtypes = []
@@ -427,6 +429,20 @@ def fe_hbm_read_probe(base, tile_ids, sink, stream=None) -> None:
         _dev(base, torch.uint8, "base", 1), base.numel() // 4096, _dev(tile_ids, torch.int32, "tile_ids", 1), n,
         _dev(sink, torch.int32, "sink", 1), _stream(stream))
     _check(rc, "fe_hbm_read_probe")
+
+
+def fe_mfma_rate_probe(operands, workgroups: int, rounds: int, sink, stream=None) -> None:
+    """Issue workgroups * 8 waves * rounds * 64 bf16 MFMAs (32x32x16) on
+    operands from the bfloat16 device tensor ``operands`` (a multiple of 8
+    elements); ``sink`` is a float32 device tensor of workgroups * 8 sums."""
+    _shape(operands, "operands", None)
+    if operands.numel() % 8:
+        raise ValueError("fe_mfma_rate_probe: operands must hold a multiple of 8 bf16 values")
+    _shape(sink, "sink", int(workgroups) * 8)
+    rc = load_library().fe_mfma_rate_probe(
+        _dev(operands, torch.bfloat16, "operands", 1), operands.numel() // 8, int(workgroups), int(rounds),
+        _dev(sink, torch.float32, "sink", 1), _stream(stream))
+    _check(rc, "fe_mfma_rate_probe")
 
 
 # ----------------------------------------------------------------------------

@@ -363,4 +363,21 @@ int fe_hbm_read_probe(const void* base, int64_t num_tiles, const int32_t* tile_i
   }
 }
 
+int fe_mfma_rate_probe(const void* operands, int n_ops, int workgroups, int rounds, float* sink, hipStream_t stream) {
+  static const char* fn = "fe_mfma_rate_probe";
+  try {
+    if (n_ops <= 0 || workgroups < 0 || rounds < 0)
+      return fail(FE_ERR_INVALID_ARG, fn, "n_ops must be positive, workgroups and rounds >= 0");
+    if (workgroups == 0) return FE_OK;
+    if (!operands || !sink) return fail(FE_ERR_NULL, fn, "operands and sink must not be NULL");
+    if (!aligned16(operands)) return fail(FE_ERR_INVALID_ARG, fn, "operands must be 16-byte aligned");
+    if (static_cast<long>(workgroups) * fe::kMfmaProbeWaves * 64 >= (1L << 31))
+      return fail(FE_ERR_UNSUPPORTED, fn, "too many workgroups for one launch");
+    const hipError_t e = fe::launch_mfma_rate_probe(operands, n_ops, workgroups, rounds, sink, stream);
+    return e == hipSuccess ? FE_OK : hip_fail(e, fn);
+  } catch (...) {
+    return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
+  }
+}
+
 }  // extern "C"

@@ -142,6 +142,14 @@ constexpr int kProbeTilesPerWave = 16;
 hipError_t launch_hbm_read_probe(const void* base, int64_t num_tiles, const int32_t* tile_ids, int n, uint32_t* sink,
                                  hipStream_t stream);
 
+// bf16 MFMA rate probe (mfma_probe.hip): workgroups of kMfmaProbeWaves waves,
+// each issuing kMfmaProbeRoundMfmas MFMAs per round and writing one float of
+// sink.
+constexpr int kMfmaProbeWaves = 8;
+constexpr int kMfmaProbeRoundMfmas = 64;
+hipError_t launch_mfma_rate_probe(const void* operands, int n_ops, int workgroups, int rounds, float* sink,
+                                  hipStream_t stream);
+
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, void* k_cache,
                             void* v_cache, int T, int num_blocks, int Hkv, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -495,6 +495,18 @@ def test_decode_noalloc_argument_errors(lib):
     assert ws(64, 32, 8, 128, 8192, 0) <= (32 << 20)
 
 
+def test_mfma_rate_probe_argument_errors(lib):
+    f = lib.fe_mfma_rate_probe
+    assert f(P, 16, 0, 4, P, None) == OK  # nothing to launch
+    assert f(None, 16, 2, 4, P, None) == NULL
+    assert f(P, 16, 2, 4, None, None) == NULL
+    assert f(P, 0, 2, 4, P, None) == INVALID
+    assert f(P, 16, -1, 4, P, None) == INVALID
+    assert f(P, 16, 2, -1, P, None) == INVALID
+    assert f(P + 4, 16, 2, 4, P, None) == INVALID
+    assert f(P, 16, 1 << 23, 4, P, None) == UNSUPPORTED
+
+
 def test_hbm_read_probe_argument_errors(lib):
     f = lib.fe_hbm_read_probe
     assert f(P, 16, P, 0, P, None) == OK  # nothing to read
