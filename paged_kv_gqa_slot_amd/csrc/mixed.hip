@@ -51,8 +51,20 @@ __global__ __launch_bounds__(MixedShape<G>::kThreads) void gqa_mixed_kernel(Mixe
   const bool is_pre = wg >= mp.n_dec_wgs;
   const int k = is_pre ? wg - mp.n_dec_wgs : wg;
   if (is_pre) {
-    const int pair = k % mp.pre_pairs;
-    pre::prefill_tile<G>(mp.pre, lds, k / mp.pre_pairs, mp.num_decode + pair / mp.pre.Hkv, pair % mp.pre.Hkv);
+    int pair, qt;
+    if (mp.pre_pairs % 8 == 0) {
+      // groups of 8 (sequence, KV head) pairs, one per XCD, with all query
+      // tiles of a group next to each other in dispatch order: the tiles
+      // that share a pair's K/V start close together and find it in L2
+      const int span = 8 * mp.pre.qtiles;
+      const int r = k % span;
+      pair = (k / span) * 8 + r % 8;
+      qt = r / 8;
+    } else {
+      pair = k % mp.pre_pairs;
+      qt = k / mp.pre_pairs;
+    }
+    pre::prefill_tile<G>(mp.pre, lds, qt, mp.num_decode + pair / mp.pre.Hkv, pair % mp.pre.Hkv);
   } else {
     int d = k;
     const int g = d % mp.dec.Hkv;
