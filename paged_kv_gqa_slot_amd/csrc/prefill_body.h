@@ -24,19 +24,21 @@
 // The MFMA sums over keys in any order as long as A and B agree, so the
 // k-slot -> key order of each PV step is chosen to match the keys the S^T
 // accumulator layout leaves in each lane (no data movement for P).
-// LDS rows are padded (K: 272 bytes, V: 320 bytes) so that the K row reads of
-// 16 consecutive keys (rows 4 banks apart) and the transposed V reads (32
-// lanes reading 64 bytes of 4 rows, rows 16 banks apart) are free of bank
-// conflicts on the 64 banks, and every LDS offset is a per-lane base plus a
-// constant.
+// K and V tiles go from global memory straight into LDS (buffer loads with
+// the LDS bit, no registers on the way), in 256-byte rows whose 16-byte
+// chunks are XOR-swizzled so that the K row reads of 16 consecutive keys and
+// the transposed V reads are free of bank conflicts on the 64 banks; every
+// LDS offset is a per-lane base plus a constant.
 //
 // Schedule.  A tile's work is split into two phases separated by workgroup
-// barriers: an MFMA phase (S^T of tile i, then O^T += V^T P^T of tile i - 1)
-// and a VALU/memory phase (softmax of tile i into P, staging tile i + 1 into
-// LDS, issuing the global loads of tile i + 2).  Each group double-buffers
-// its K/V tiles in LDS.  With two groups the second runs one phase behind the
-// first, so on every SIMD one wave's MFMAs overlap the other wave's softmax
-// instead of both waves contending for the same unit at the same time.
+// barriers: an MFMA phase (S^T of tile i, then O^T += V^T P^T of tile i - 1),
+// run at the highest wave priority, and a VALU/memory phase (the copies of V
+// of tile i + 1 and K of tile i + 2 into the buffers the MFMA phase just
+// finished reading, then the softmax of tile i into P).  Each group has two
+// K and two V buffers in LDS.  With two groups the second runs one phase
+// behind the first, so on every SIMD one wave's MFMAs overlap the other
+// wave's softmax instead of both waves contending for the same unit at the
+// same time.
 #pragma once
 
 #include <math.h>
