@@ -246,12 +246,17 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
  *                  1 = each workgroup walks its keys with one group of waves
  *                  (two workgroups fit on a compute unit);
  *                  2 = two wave groups split the keys and merge by
- *                  log-sum-exp (one workgroup per compute unit); valid only
- *                  for Hq/Hkv <= 4, else FE_ERR_UNSUPPORTED.
- *                  Other values: FE_ERR_INVALID_ARG.
+ *                  log-sum-exp (one workgroup per compute unit);
+ *                  3 = two wave groups take two consecutive query tiles over
+ *                  one shared stream of K/V tiles (one workgroup per
+ *                  compute unit, half as many workgroups);
+ *                  2 is valid only for Hq/Hkv <= 4 and 3 only for Hq/Hkv in
+ *                  {1, 2, 4}, else FE_ERR_UNSUPPORTED.  Other values:
+ *                  FE_ERR_INVALID_ARG.
  * The automatic choice takes 2 when the launch has at most one workgroup
- * per compute unit and 1 otherwise.  The shapes differ only in the order
- * of fp32 additions, so results agree within rounding, not bit for bit.
+ * per compute unit, 3 above that (1 when a chunk has a single query tile or
+ * Hq/Hkv = 3), and 1 for Hq/Hkv > 4.  The shapes differ only in the order of fp32
+ * additions, so results agree within rounding, not bit for bit.
  * Source: as fe_paged_gqa_prefill_chunk.
  */
 int fe_paged_gqa_prefill_chunk_ex(void* out, float* lse, const void* q, const int32_t* query_start_loc,

@@ -315,7 +315,8 @@ def fe_paged_gqa_prefill_chunk_ex(out, lse, q, query_start_loc, k_cache, v_cache
                                   max_q_len: int, max_context_len: int, scale: float, key_groups: int,
                                   stream=None) -> None:
     """fe_paged_gqa_prefill_chunk with the tile shape chosen by the caller
-    (key_groups 0 automatic, 1 or 2 wave groups per workgroup)."""
+    (key_groups 0 automatic, 1 or 2 wave groups over the keys, 3 two query
+    tiles over one K/V stream)."""
     _shape(q, "q", None, None, None)
     total_q, Hq, D = q.shape
     NB, Hkv, BS, _ = _pools(k_cache, v_cache)

@@ -198,7 +198,7 @@ int prefill_chunk(const char* fn, void* out, float* lse, const void* q, const in
                   const int32_t* context_lens, int B, int total_q, int max_q_len, int Hq, int Hkv, int D, int BS,
                   int num_blocks, int max_context_len, float scale, int key_groups, hipStream_t stream) {
   try {
-    if (key_groups < 0 || key_groups > 2) return fail(FE_ERR_INVALID_ARG, fn, "key_groups must be 0, 1 or 2");
+    if (key_groups < 0 || key_groups > 3) return fail(FE_ERR_INVALID_ARG, fn, "key_groups must be 0, 1, 2 or 3");
     if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
       return fail(FE_ERR_INVALID_ARG, fn,
                   "B, total_q, max_q_len, max_context_len must be >= 0; num_blocks, max_blocks_per_seq positive");
@@ -206,6 +206,8 @@ int prefill_chunk(const char* fn, void* out, float* lse, const void* q, const in
     if (!isfinite(scale)) return fail(FE_ERR_INVALID_ARG, fn, "scale must be finite");
     if (key_groups == 2 && !fe::prefill_two_key_groups_supported(Hq / Hkv))
       return fail(FE_ERR_UNSUPPORTED, fn, "key_groups 2 needs Hq/Hkv <= 4");
+    if (key_groups == 3 && !fe::prefill_query_tile_pairs_supported(Hq / Hkv))
+      return fail(FE_ERR_UNSUPPORTED, fn, "key_groups 3 needs Hq/Hkv in {1, 2, 4}");
     if (B == 0 || total_q == 0) return FE_OK;
     if (!out || !q || !query_start_loc || !k_cache || !v_cache || !block_tables || !context_lens)
       return fail(FE_ERR_NULL, fn,

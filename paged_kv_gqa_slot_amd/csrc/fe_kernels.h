@@ -67,7 +67,7 @@ struct PrefillArgs {
   const int32_t* context_lens;
   int B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len;
   float scale;
-  int key_groups = 0;  // prefill tile: 0 automatic, 1 or 2 key groups per workgroup
+  int key_groups = 0;  // prefill tile: 0 automatic, 1 or 2 key groups, 3 two query tiles over one K/V stream
 };
 
 // Mixed decode/prefill launch plan.  The decode sequences are split into
@@ -154,7 +154,8 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t*
                             void* v_cache, int T, int num_blocks, int Hkv, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-bool prefill_two_key_groups_supported(int G);  // key_groups = 2 is valid for this Hq / Hkv
+bool prefill_two_key_groups_supported(int G);    // key_groups = 2 is valid for this Hq / Hkv
+bool prefill_query_tile_pairs_supported(int G);  // key_groups = 3 is valid for this Hq / Hkv
 hipError_t launch_mixed(const MixedArgs& a, hipStream_t stream);
 hipError_t launch_qk_norm_rope(const NormRopeArgs& a, hipStream_t stream);
 hipError_t launch_sampler(const SamplerArgs& a, hipStream_t stream);

@@ -52,10 +52,22 @@ hipError_t launch_g(const PrefillArgs& a, const PrefillParams& prm, hipStream_t 
   const long grid = static_cast<long>(copy.qtiles) * prm.Hkv * prm.B;
   if (grid == 0) return hipSuccess;
   if constexpr (Shape<G>::KS == 2) {
-    const int ks = a.key_groups != 0 ? a.key_groups : (grid > kCuCount ? 1 : 2);
+    // two key groups per tile while the grid fits the CUs; beyond that, two
+    // query tiles per workgroup over one K/V stream
+    constexpr bool kPairs = Shape<G>::W == 4;  // (G = 3 runs groups of 3 waves)
+    const int ks =
+        a.key_groups != 0 ? a.key_groups : (grid > kCuCount ? (kPairs && copy.qtiles > 1 ? 3 : 1) : 2);
     if (ks == 1) return launch_shape<G, 1>(copy, grid, stream);
+    if constexpr (kPairs) {
+      if (ks == 3) {
+        const long pairs_grid = static_cast<long>((copy.qtiles + 1) / 2) * prm.Hkv * prm.B;
+        return launch_shape<G, 3>(copy, pairs_grid, stream);
+      }
+    } else {
+      if (ks == 3) return hipErrorInvalidValue;
+    }
   } else {
-    if (a.key_groups == 2) return hipErrorInvalidValue;
+    if (a.key_groups >= 2) return hipErrorInvalidValue;
   }
   return launch_shape<G, 0>(copy, grid, stream);
 }
@@ -65,6 +77,7 @@ hipError_t launch_g(const PrefillArgs& a, const PrefillParams& prm, hipStream_t 
 static_assert(Shape<1>::KS == 2 && Shape<3>::KS == 2 && Shape<4>::KS == 2 && Shape<5>::KS == 1,
               "two key groups exactly for Hq/Hkv <= 4");
 bool prefill_two_key_groups_supported(int G) { return G >= 1 && G <= 4; }
+bool prefill_query_tile_pairs_supported(int G) { return G == 1 || G == 2 || G == 4; }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const PrefillParams prm = make_prefill_params(a);

@@ -79,16 +79,27 @@ struct PrefillParams {
 };
 
 // KSel = 0 takes the default number of key groups (two when a group has at
-// most 4 waves); KSel = 1 forces one group, half the LDS of two.
+// most 4 waves); KSel = 1 forces one group, half the LDS of two; KSel = 2
+// forces two.  KSel = 3 (kPair) also has two groups, but they take two
+// consecutive query tiles over one shared stream of K/V tiles instead of
+// splitting the keys (for grids with more tiles than CUs).
 template <int G, int KSel = 0>
 struct Shape {
   static constexpr int W = (G <= 4 && 4 % G == 0) ? 4 : G;  // waves per group
-  static constexpr int KS = KSel != 0 ? KSel : (W <= 4 ? 2 : 1);  // groups splitting the keys
-  static constexpr int QT = 32 * W / G;                     // query rows per workgroup
+  static constexpr bool kPair = KSel == 3;
+  static constexpr int KS = kPair ? 2 : (KSel != 0 ? KSel : (W <= 4 ? 2 : 1));  // wave groups
+  static constexpr int QT = 32 * W / G;                     // query rows per group
   static constexpr int kThreads = 64 * W * KS;
   // a 64-key tile is 4 KV blocks; wave w of a group stages blocks w, w + W, ...
   static constexpr int kStageBlocks = (4 + W - 1) / W;
-  static constexpr int kLdsBytes = KS * kGroupBytes;
+  // K and V buffers: two per group, or three shared ones (kPair: a tile is
+  // read by both groups, one phase apart, so a buffer frees one phase later)
+  static constexpr int kBufs = kPair ? 3 : 2;
+  static constexpr int kLdsBytes = kPair ? 2 * kBufs * kTileBytes : KS * kGroupBytes;
+  // tiles ahead of the current one whose V and K copies a step issues
+  static constexpr int kLeadV = kPair ? 2 : 1;
+  static constexpr int kLeadK = kPair ? 3 : 2;
+  static_assert(!kPair || W == 4, "paired query tiles are built for groups of 4 waves");
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -138,7 +149,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave_all = uniform(tid >> 6);
-  const int grp = wave_all / S::W;  // which half of the key range
+  const int grp = wave_all / S::W;  // which half of the key range (kPair: which query tile)
   const int wave = wave_all % S::W;
   const int col = lane & 31;   // this lane's query within the wave's 32
   const int half = lane >> 5;  // which 8-dim / 4-key half of an MFMA operand
@@ -146,8 +157,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   const int q0 = p.query_start_loc[b];
   int C = p.query_start_loc[b + 1] - q0;
   C = C < 0 ? 0 : (C > p.max_q_len ? p.max_q_len : C);
-  const int i0 = qt * S::QT;
-  if (i0 >= C) return;
+  // first query of the workgroup and of this group (kPair: tiles 2 qt and 2 qt + 1)
+  const int wg_i0 = (S::kPair ? 2 * qt : qt) * S::QT;
+  const int i0 = wg_i0 + (S::kPair ? grp * S::QT : 0);
+  if (wg_i0 >= C) return;  // (kPair: a second tile past the chunk still stages the first one's K/V)
   int L = p.context_lens[b];
   L = L < 0 ? 0 : (L > p.ctx_cap ? p.ctx_cap : L);
 
@@ -176,21 +189,22 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   }
 
   // keys this workgroup needs: 0 .. last visible position of its last query
-  const int last_q = min(i0 + S::QT, C) - 1;
+  const int last_q = min(wg_i0 + (S::kPair ? 2 : 1) * S::QT, C) - 1;
   const int kv_end = max(0, min(L, L - C + last_q + 1));
   const int n_tiles = (kv_end + kKeysPerTile - 1) / kKeysPerTile;
   const int diag_from = max(0, L - C + i0 + 1);  // keys beyond this need the causal mask for some row
   const int n_plain = min(n_tiles, diag_from / kKeysPerTile);  // tiles needing no mask
-  // group 0 takes tiles [0, nA), group 1 tiles [nA, n_tiles)
-  const int nA = S::KS == 2 ? (n_tiles + 1) / 2 : n_tiles;
-  const int t_first = grp * nA;
-  const int t_end = grp == 0 ? nA : n_tiles;
+  // group 0 takes tiles [0, nA), group 1 tiles [nA, n_tiles) (kPair: both take all)
+  const int nA = S::KS == 2 && !S::kPair ? (n_tiles + 1) / 2 : n_tiles;
+  const int t_first = S::kPair ? 0 : grp * nA;
+  const int t_end = grp == 0 || S::kPair ? nA : n_tiles;
 
   const int32_t* bt = p.block_tables + static_cast<size_t>(b) * p.max_blocks;
   const size_t blk_stride = static_cast<size_t>(p.Hkv) * kTileElems;
   const uint16_t* kg = p.k_cache + static_cast<size_t>(g) * kTileElems;
   const uint16_t* vg = p.v_cache + static_cast<size_t>(g) * kTileElems;
-  const int grp_base = grp * kGroupBytes;  // this group's K tiles 0, 1, then V tiles 0, 1
+  // this group's K tiles, then its V tiles (kPair: the shared ones)
+  const int grp_base = S::kPair ? 0 : grp * kGroupBytes;
   const int n_g = t_end - t_first;         // this group's tiles
 
   // Staging: wave w copies blocks w, w + W, ... of each 64-key tile, each a
@@ -222,9 +236,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     ids_chunk = chunk;
   };
   // blocks this wave stages per tile, and the LDS-direct loads that makes
+  // (kPair: the second group stages the shared tiles, the first stages none)
+  const bool stager = !S::kPair || grp == 1;
   int n_stage = 0;
 #pragma unroll
-  for (int i = 0; i < S::kStageBlocks; ++i) n_stage += wave + i * S::W < 4 ? 1 : 0;
+  for (int i = 0; i < S::kStageBlocks; ++i) n_stage += stager && wave + i * S::W < 4 ? 1 : 0;
   // Global byte offsets of this lane's 16 bytes within the j-th 1 KiB run
   // (rows 4 j .. 4 j + 3 of a block; the 1024 j itself is the instruction
   // offset), for the swizzles above: a block's rows are rows 16 bl + r of
@@ -270,7 +286,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     for (int i = 0; i < S::kStageBlocks; ++i) {
       const int bl = wave + i * S::W;
       if (bl < 4)
-        lds_direct_tile(vg + off[i], bytes[i], lds_addr + (2 + vb) * kTileBytes + bl * 4096, vvo, vvo, vvo, vvo);
+        lds_direct_tile(vg + off[i], bytes[i], lds_addr + (S::kBufs + vb) * kTileBytes + bl * 4096, vvo, vvo, vvo,
+                        vvo);
     }
   };
   // every copy this wave issued before its latest 2 n_stage tiles has landed
@@ -294,7 +311,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   int vra[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
-    vra[d] = grp_base + 2 * kTileBytes + (4 * (gq >> 1) + (src >> 2)) * kRowBytes +
+    vra[d] = grp_base + S::kBufs * kTileBytes + (4 * (gq >> 1) + (src >> 2)) * kRowBytes +
              ((2 * (gq & 1) + ((src & 3) >> 1) + 4 * (d ^ (src >> 2))) << 4) + 8 * (src & 1);
 
   f32x16_t o_acc[4];  // O^T, dim block d: lane holds query col, dims 32 d + 8 (i / 4) + 4 half + i % 4
@@ -416,14 +433,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
 
-  // MFMA phase of local tile i (K buffer bufc): S^T of tile i and, when pvc,
-  // O^T += V^T P^T of tile i - 1 (V buffer 1 - bufc).  One basic block; the
+  // MFMA phase of local tile i (K buffer bufc = i mod kBufs): S^T of tile i
+  // and, when pvc, O^T += V^T P^T of tile i - 1 (the V buffer before bufc,
+  // cyclically).  One basic block; the
   // scheduling groups keep four MFMA operands in flight from LDS so the read
   // latency hides behind the MFMAs (16 K reads of 16 bytes for S^T, then two
   // 8-byte transposed V reads per PV MFMA).
   auto mphase = [&](auto bufc, auto pvc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    using Other = std::integral_constant<int, 1 - buf>;
+    using Other = std::integral_constant<int, (buf + S::kBufs - 1) % S::kBufs>;
     qk(bufc);
     if constexpr (decltype(pvc)::value) {
       pv(Other{});
@@ -452,6 +470,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   // barrier.  A copy thus has a phase and a half to land.  The O rescale in
   // the softmax sees O with tile i - 1 already accumulated, as the online
   // softmax requires.
+  // kPair: the three shared buffers of each kind hold tiles i mod 3.  Group 0
+  // reads a tile one phase before group 1, so a buffer frees after group 1's
+  // MFMA phase; group 1 (the stager) then copies V of tile i + 2 and K of
+  // tile i + 3 in its VALU phase of tile i, into the buffers of tiles i - 1
+  // and i, and waits for the copies of the step before, two phases ahead of
+  // group 0's first read of them.
   size_t v_off[S::kStageBlocks];
   int v_bytes[S::kStageBlocks];
   auto step = [&](auto bufc, auto pvc, int i) __attribute__((always_inline)) {
@@ -464,14 +488,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     mphase(bufc, pvc);
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
-    stage_v(1 - buf, v_off, v_bytes);  // tile i + 1 (located with its K copy)
-    locate(t_first + i + 2);
+    if (stager) {
+      stage_v((buf + S::kLeadV) % S::kBufs, v_off, v_bytes);  // tile i + kLeadV (located with its K copy)
+      locate(t_first + i + S::kLeadK);
 #pragma unroll
-    for (int k = 0; k < S::kStageBlocks; ++k) {
-      v_off[k] = src_off[k];
-      v_bytes[k] = src_bytes[k];
+      for (int k = 0; k < S::kStageBlocks; ++k) {
+        v_off[k] = src_off[k];
+        v_bytes[k] = src_bytes[k];
+      }
+      stage_k(buf);  // tile i + kLeadK, into the buffer of tile i
     }
-    stage_k(buf);  // tile i + 2
     softmax(t_first + i);
     wait_previous();
     __syncthreads();
@@ -481,37 +507,61 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   // memory round trip, settled on every path here so that no later barrier
   // waits on memory.  Each key group then copies K of its tiles 0 and 1 and V
   // of tile 0 and waits for K of tile 0 before the barriers, so the two
-  // groups' first round trips overlap.  Group 1 then takes one extra barrier,
-  // which puts it one phase behind group 0.  Copies of tiles past a group's
-  // range read nothing and write zeros into a buffer nobody reads.
-  load_ids(0);
-  wait_vm<0>();
-  locate(t_first);
-  stage_k(0);
-  stage_v(0, src_off, src_bytes);
-  locate(t_first + 1);
+  // groups' first round trips overlap (kPair: the stager copies K of tiles
+  // 0 - 2 and V of tiles 0 - 1 and waits for all of them).  Group 1 then
+  // takes one extra barrier, which puts it one phase behind group 0.  Copies
+  // of tiles past a group's range read nothing and write zeros into a buffer
+  // nobody reads.
+  if (stager) {
+    load_ids(0);
+    wait_vm<0>();
 #pragma unroll
-  for (int k = 0; k < S::kStageBlocks; ++k) {
-    v_off[k] = src_off[k];
-    v_bytes[k] = src_bytes[k];
+    for (int t = 0; t < S::kLeadK; ++t) {
+      locate(t_first + t);
+      stage_k(t);
+      if (t < S::kLeadV) stage_v(t, src_off, src_bytes);
+      if (t == S::kLeadV) {
+#pragma unroll
+        for (int k = 0; k < S::kStageBlocks; ++k) {
+          v_off[k] = src_off[k];
+          v_bytes[k] = src_bytes[k];
+        }
+      }
+    }
+    if (S::kPair)
+      wait_vm<0>();
+    else
+      wait_previous();
   }
-  stage_k(1);
-  wait_previous();
   if (S::KS == 2 && grp == 1) __syncthreads();
   __syncthreads();
+  using B2 = std::integral_constant<int, 2>;
   if (n_g > 0) step(B0{}, std::false_type{}, 0);  // the first tile has no PV of a previous one
   int i = 1;
-  for (; i + 1 < n_g; i += 2) {
-    step(B1{}, std::true_type{}, i);
-    step(B0{}, std::true_type{}, i + 1);
+  if constexpr (S::kBufs == 2) {
+    for (; i + 1 < n_g; i += 2) {
+      step(B1{}, std::true_type{}, i);
+      step(B0{}, std::true_type{}, i + 1);
+    }
+    if (i < n_g) step(B1{}, std::true_type{}, i);
+  } else {
+    for (; i + 2 < n_g; i += 3) {
+      step(B1{}, std::true_type{}, i);
+      step(B2{}, std::true_type{}, i + 1);
+      step(B0{}, std::true_type{}, i + 2);
+    }
+    if (i < n_g) step(B1{}, std::true_type{}, i++);
+    if (i < n_g) step(B2{}, std::true_type{}, i++);
   }
-  if (i < n_g) step(B1{}, std::true_type{}, i);
   // the last tile's PV
   if (n_g > 0) {
-    if ((n_g - 1) & 1)
-      pv(B1{});
-    else
+    const int lb = (n_g - 1) % S::kBufs;
+    if (lb == 0)
       pv(B0{});
+    else if (lb == 1)
+      pv(B1{});
+    else if constexpr (S::kBufs == 3)
+      pv(B2{});
   }
   // the copies past the range land before LDS is reused below
   wait_vm<0>();
@@ -524,7 +574,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
     lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  if (S::KS == 2) {
+  if (S::KS == 2 && !S::kPair) {
     // group 1 hands (m, lsum, O^T) to group 0 through LDS (tiles are done)
     float* xs = reinterpret_cast<float*>(lds) + (wave * 64 + lane) * 66;
     if (grp == 1) {

@@ -112,7 +112,7 @@ class DeviceWorkload:
 
     def prefill(self, max_q_len=None, key_groups=None):
         """fe_paged_gqa_prefill_chunk, or fe_paged_gqa_prefill_chunk_ex with
-        the given tile shape (key_groups 0, 1 or 2)."""
+        the given tile shape (key_groups 0, 1, 2 or 3)."""
         w = self.w
         total_q = self.q.shape[0]
         out = torch.full((total_q, w.Hq, 128), float("nan"), dtype=torch.bfloat16, device=self.dev)

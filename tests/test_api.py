@@ -178,11 +178,14 @@ def pre_ex(lib, key_groups, **kw):
 
 def test_prefill_ex_key_groups_checks(lib):
     # checked before anything is enqueued; B = 0 makes every valid call a no-op
-    for kg in (0, 1, 2):
+    for kg in (0, 1, 2, 3):
         assert pre_ex(lib, kg, B=0) == OK
-    assert pre_ex(lib, 3, B=0) == INVALID
+    assert pre_ex(lib, 4, B=0) == INVALID
     assert pre_ex(lib, -1, B=0) == INVALID
     assert pre_ex(lib, 2, B=0, Hq=40, Hkv=8) == UNSUPPORTED  # two groups exist only for Hq/Hkv <= 4
+    assert pre_ex(lib, 3, B=0, Hq=40, Hkv=8) == UNSUPPORTED
+    assert pre_ex(lib, 3, B=0, Hq=24, Hkv=8) == UNSUPPORTED  # Hq/Hkv = 3 runs groups of 3 waves
+    assert pre_ex(lib, 3, B=0, Hq=16, Hkv=8) == OK
     assert pre_ex(lib, 1, B=0, Hq=64, Hkv=8) == OK
     assert pre_ex(lib, 2, B=0, Hq=24, Hkv=8) == OK
     # the other checks are those of fe_paged_gqa_prefill_chunk

@@ -49,13 +49,14 @@ def run_prefill(w, dev, label, rows=None, lens_override=None, key_groups=None):
 # key group through fe_paged_gqa_prefill_chunk_ex.  Forcing one group where
 # it is already the default would repeat the automatic case, so those
 # combinations are not generated.
-KEY_GROUPS = [None, 1]
+KEY_GROUPS = [None, 1, 3]
 
 
 def tile_cases(Gs):
-    """(G, key_groups) pairs: both tiles where two key groups are the
-    default (Hq/Hkv <= 4), the automatic tile alone above."""
-    return [(G, kg) for G in Gs for kg in KEY_GROUPS if not (kg == 1 and G > 4)]
+    """(G, key_groups) pairs: every tile each group size has (Hq/Hkv <= 4:
+    the automatic two key groups and one group; Hq/Hkv in {1, 2, 4} also two
+    query tiles over one K/V stream), the automatic tile alone above 4."""
+    return [(G, kg) for G in Gs for kg in KEY_GROUPS if not (kg == 1 and G > 4) and not (kg == 3 and G not in (1, 2, 4))]
 
 
 @pytest.mark.parametrize("G,kg", tile_cases([1, 2, 3, 4, 5, 6, 7, 8]))
@@ -106,7 +107,8 @@ def test_prefill_tile_counts(dev, G, kg):
     run_prefill(w, dev, f"tile counts G={G} key_groups={kg}", key_groups=kg)
 
 
-@pytest.mark.parametrize("G,lens,kg", [(4, [9000, 8300], None), (4, [9000, 8300], 1), (8, [4500, 4200], None)])
+@pytest.mark.parametrize("G,lens,kg", [(4, [9000, 8300], None), (4, [9000, 8300], 1), (4, [9000, 8300], 3),
+                                      (8, [4500, 4200], None)])
 def test_prefill_long_key_range(dev, G, lens, kg):
     """More than 64 tiles of keys per wave group, so the kernel's per-wave
     list of staged block ids is reloaded mid-sequence."""
