@@ -22,12 +22,24 @@ template <int G, int KSel>
 __global__ __launch_bounds__((Shape<G, KSel>::kThreads)) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 gqa_prefill_chunk_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[Shape<G, KSel>::kLdsBytes];
-  // Workgroups are dispatched round-robin over the 8 XCDs (id mod 8).  The
-  // query tile is the slowest-varying index, so all tiles of one (sequence,
-  // KV head) pair share an XCD and read its K/V through one L2.
+  // Workgroups are dispatched round-robin over the 8 XCDs (id mod 8).  All
+  // query tiles of one (sequence, KV head) pair go to one XCD and read its
+  // K/V through one L2; and they sit next to each other in dispatch order,
+  // in groups of 8 pairs (one per XCD), so that on a grid larger than the
+  // GPU they also run at the same time and find each other's K/V there.
   const int pairs = p.B * p.Hkv;
-  const int pair = blockIdx.x % pairs;
-  prefill_tile<G, KSel>(p, lds, blockIdx.x / pairs, pair / p.Hkv, pair % p.Hkv);
+  const int units = gridDim.x / pairs;  // query tiles (or tile pairs) per sequence in this launch
+  int pair, qt;
+  if (pairs % 8 == 0) {
+    const int span = 8 * units;
+    const int r = blockIdx.x % span;
+    pair = (blockIdx.x / span) * 8 + r % 8;
+    qt = r / 8;
+  } else {
+    pair = blockIdx.x % pairs;
+    qt = blockIdx.x / pairs;
+  }
+  prefill_tile<G, KSel>(p, lds, qt, pair / p.Hkv, pair % p.Hkv);
 }
 
 template <int G, int KSel>
