@@ -289,7 +289,9 @@ size_t fe_paged_gqa_mixed_workspace_size(int num_decode, int Hq, int Hkv, int D,
  *   fe_paged_gqa_prefill_chunk, over all B sequences.
  *   max_q_len      host-side upper bound of the prefill chunks' lengths
  *   num_partitions split-K factor of the decode rows (0 = automatic: ranges
- *                  of 64 blocks), at most 256 blocks per range as in decode
+ *                  of at least 64 blocks, and no more than about 6 decode
+ *                  items (sequence, KV head, partition) per compute unit),
+ *                  at most 256 blocks per range as in decode
  *   workspace      device scratch of at least
  *                  fe_paged_gqa_mixed_workspace_size(...) bytes (NULL when
  *                  that is 0), owned by the caller.  It must be zero-filled

@@ -82,9 +82,14 @@ struct MixedPlan {
   size_t lse_part_offset;
 };
 
-// Automatic decode partitions of a mixed launch: ranges of 64 blocks (1024
-// tokens), since the prefill tiles of the same grid already occupy the GPU.
-constexpr int kMixedAutoPartBlocks = 64;
+// Automatic decode partitions of a mixed launch: ranges of at least
+// kMixedMinPartBlocks blocks (1024 tokens), and no more partitions than
+// about kMixedItemsPerCu decode items per CU.  The launch runs one workgroup
+// per CU (every workgroup reserves the prefill tile's LDS and registers), so
+// each decode item's fixed start and split-merge cost is paid in series on
+// its CU; with many decode rows, fewer and longer items pay it less often.
+constexpr int kMixedMinPartBlocks = 64;
+constexpr int kMixedItemsPerCu = 6;
 
 bool plan_mixed(int num_decode, int Hq, int Hkv, int max_context_len, int num_partitions, MixedPlan* plan);
 

@@ -21,6 +21,8 @@
 namespace fe {
 namespace {
 
+constexpr int kCuCount = 256;
+
 struct MixedParams {
   pre::PrefillParams pre;
   dec::DecodeParams dec;
@@ -99,7 +101,14 @@ bool plan_mixed(int num_decode, int Hq, int Hkv, int max_context_len, int num_pa
   const int nblk_max = (max_context_len + kBlockSize - 1) / kBlockSize;
   MixedPlan r{1, kMaxPartBlocks, 0, 0, 0};
   if (nblk_max > 0 && num_decode > 0) {
-    int P = num_partitions > 0 ? num_partitions : (nblk_max + kMixedAutoPartBlocks - 1) / kMixedAutoPartBlocks;
+    int P = num_partitions;
+    if (P <= 0) {
+      const long pairs = static_cast<long>(num_decode) * Hkv;
+      const long by_items = (static_cast<long>(kMixedItemsPerCu) * kCuCount + pairs / 2) / pairs;
+      const long by_len = (nblk_max + kMixedMinPartBlocks - 1) / kMixedMinPartBlocks;
+      const long pa = by_items < by_len ? by_items : by_len;
+      P = static_cast<int>(pa < 1 ? 1 : pa);
+    }
     if (P > nblk_max) P = nblk_max;
     int part_blocks = (nblk_max + P - 1) / P;
     if (part_blocks > kMaxPartBlocks) part_blocks = kMaxPartBlocks;

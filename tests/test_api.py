@@ -253,6 +253,9 @@ def test_mixed_workspace_plan(lib):
     # counters + fp32 partials + their LSEs
     need = ws(4, 32, 8, 128, 8192, 0)
     assert need >= 4 * 8 * 4 + 4 * 32 * 8 * (128 + 1) * 4
+    # 60 decode rows x 8 KV heads: about 6 items per compute unit -> 3 partitions of 160 blocks
+    need60 = ws(60, 32, 8, 128, 7665, 0)
+    assert 60 * 32 * 3 * (128 + 1) * 4 <= need60 < 60 * 32 * 4 * (128 + 1) * 4
     assert ws(4, 32, 8, 128, 4096, 1) == 0          # one range of 256 blocks
     assert ws(4, 32, 8, 128, 8192, 1) > 0           # a range holds at most 256 blocks: raised to 2
     assert ws(4, 30, 8, 128, 8192, 0) == ctypes.c_size_t(-1).value
