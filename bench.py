@@ -15,7 +15,9 @@ decode call; every other mode is timed and reported beside it (--eager skips
 the graphs).  `roofline` is for the decode call, timed with HIP events on the
 stream its kernels run on, against the 8 TB/s peak and a same-run read
 ceiling of the kernel's own load form; `cpu_baseline` is the fp64 oracle on
-the host.
+the host.  Each timed loop follows --settle-ms (100) ms of untimed launches
+of the same step, then its --warmup steps: after an idle spell the chip's
+clock takes 10-30 ms of load to settle.
 
 Other workloads (--workload): the chunked-prefill one reports TFLOP/s against
 the bf16 MFMA peak; the mixed one (decode rows and prefill chunks in one
@@ -39,6 +41,33 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA peak
 DEFAULT_WORKLOAD = "qwen3_4b_b64_ctx1024-8192"
 
 
+def settle(torch, fn, ms: float) -> int:
+    """Runs fn back to back, untimed, for `ms` milliseconds of wall time
+    before a timed loop.  After an idle spell (workload generation, graph
+    capture) the chip's power controller takes 10-30 ms of sustained load to
+    settle its clock: the first steps after idle run up to 30% slower than
+    the settled ones (decode 200-216 against 189 us, the mixed step 355
+    against 264 us) before they recover, so a handful of warm-up steps alone
+    leaves the timed loop on that transient.  Launches go in batches of about
+    2 ms with a synchronisation between them, so the host never queues far
+    ahead of the wall-clock budget.  Returns the number of calls made."""
+    if ms <= 0:
+        return 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n, batch = 0, 1
+    while True:
+        t = time.perf_counter()
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        n += batch
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return n
+        dt = max(time.perf_counter() - t, 1e-6)
+        batch = max(1, min(4 * batch, int(batch * 2e-3 / dt)))
+
+
 def spread(per_ms):
     """p10 / p50 / p90 of sorted per-launch times (ms)."""
     n = len(per_ms)
@@ -46,7 +75,7 @@ def spread(per_ms):
     return {"p10_ms": round(pick(0.1), 5), "p50_ms": round(pick(0.5), 5), "p90_ms": round(pick(0.9), 5)}
 
 
-def streaming_read_ceiling(torch, dev, fe):
+def streaming_read_ceiling(torch, dev, fe, settle_ms: float):
     """Same-run HBM read ceiling of the decode kernels' own load form
     (fe_hbm_read_probe: whole 4 KiB tiles, non-temporal 16-byte buffer loads,
     one wave per tile) over a 4 GiB buffer, far beyond the 256 MB last-level
@@ -62,6 +91,7 @@ def streaming_read_ceiling(torch, dev, fe):
     stream = torch.cuda.current_stream()
     res = {}
     for name, ids in orders.items():
+        settle(torch, lambda: fe.fe_hbm_read_probe(base, ids, sink), settle_ms)
         for _ in range(2):
             fe.fe_hbm_read_probe(base, ids, sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -78,7 +108,7 @@ def streaming_read_ceiling(torch, dev, fe):
                       "same run (sequential order beside it)"}
 
 
-def sustained_mfma_ceiling(torch, dev, fe):
+def sustained_mfma_ceiling(torch, dev, fe, settle_ms: float):
     """Same-run bf16 MFMA rate of the prefill tile's instruction
     (fe_mfma_rate_probe: v_mfma_f32_32x32x16_bf16 back to back, two waves per
     SIMD, every CU busy, operands of seeded random data) over about a
@@ -90,6 +120,7 @@ def sustained_mfma_ceiling(torch, dev, fe):
     wgs, rounds = 1024, 256  # 4 workgroups per CU
     sink = torch.empty(wgs * 8, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    settle(torch, lambda: fe.fe_mfma_rate_probe(ops, wgs, rounds, sink), settle_ms)
     for _ in range(2):
         fe.fe_mfma_rate_probe(ops, wgs, rounds, sink)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -314,6 +345,7 @@ def time_calls(args, torch, step):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / args.steps
 
+    settle(torch, step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     eager_ms = batched(step)
@@ -322,9 +354,11 @@ def time_calls(args, torch, step):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
+        settle(torch, graph.replay, args.settle_ms)
         for _ in range(args.warmup):
             graph.replay()
         graph_ms = batched(graph.replay)
+    settle(torch, fn, args.settle_ms)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for e0, e1 in evs:
         e0.record(stream)
@@ -370,7 +404,7 @@ def bench_norm_rope(args, w, fe, inputs, torch, dev):
             "kernel": "fe_qk_norm_rope_append (qk_norm_rope_kernel)", "per_launch_bytes": nbytes,
             "avg_ms": round(avg, 5), "per_call_avg_ms": round(sum(per) / len(per), 5),
             "median_ms": round(per[len(per) // 2], 5), **spread(per)}
-    ceil = streaming_read_ceiling(torch, dev, fe)
+    ceil = streaming_read_ceiling(torch, dev, fe, args.settle_ms)
     roof["streaming_read_ceiling"] = ceil
     roof["frac_of_streaming_ceiling"] = round(achieved / ceil["GBps"], 4)
     calibrate_copies(args, torch, dev)
@@ -392,6 +426,7 @@ def bench_norm_rope(args, w, fe, inputs, torch, dev):
                          f"{reps} repetitions, {el / reps * 1e3:.1f} ms each"}
     cfg = {"workload": f"norm_rope:{w.spec.name}", "tokens": T, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": 128,
            "block_size": 16, "table_rows": int(c.cos_sin.shape[0]), "seed": w.seed, "launch": launch,
+           "settle_ms": args.settle_ms,
            "eager_ms_per_step": round(eager_ms, 5),
            "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5)}
     rec = {"metric": "fused QK-RMSNorm + rotary + KV append, achieved HBM GB/s, Qwen3-4B shape",
@@ -427,7 +462,7 @@ def bench_sampler(args, fe, inputs, torch, dev):
             "kernel": "fe_sampler_softmax_argmax (sampler_partial_kernel + sampler_write_kernel)",
             "per_launch_bytes": nbytes, "avg_ms": round(avg, 5), "per_call_avg_ms": round(sum(per) / len(per), 5),
             "median_ms": round(per[len(per) // 2], 5), **spread(per)}
-    ceil = streaming_read_ceiling(torch, dev, fe)
+    ceil = streaming_read_ceiling(torch, dev, fe, args.settle_ms)
     roof["streaming_read_ceiling"] = ceil
     roof["frac_of_streaming_ceiling"] = round(achieved / ceil["GBps"], 4)
     calibrate_copies(args, torch, dev)
@@ -446,7 +481,7 @@ def bench_sampler(args, fe, inputs, torch, dev):
         cpu = {"value": round(nbytes / (el / reps) / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"fp64 oracle over all {B} rows of {V} logits, {reps} repetitions, {el / reps * 1e3:.1f} ms each"}
     cfg = {"workload": f"sampler:qwen3_vocab{V}_b{B}", "batch": B, "vocab": V, "seed": args.seed or 1,
-           "launch": launch, "eager_ms_per_step": round(eager_ms, 5),
+           "launch": launch, "settle_ms": args.settle_ms, "eager_ms_per_step": round(eager_ms, 5),
            "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5)}
     rec = {"metric": "fp32 softmax + argmax over the vocabulary, achieved HBM GB/s", "value":
            round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -464,6 +499,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partitions", type=int, default=0, help="decode split-K factor (0 = automatic)")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed back-to-back launches before each timed loop, in ms of wall time, so the "
+                         "chip's clock has settled under the load (0 = none)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -574,7 +612,8 @@ def main():
     # here); a decode step with one new token per sequence uses the fused
     # append + decode call.  Every mode is timed and reported in `config`.
     launch = "hip_graph" if len(L) > 1 and not args.eager else "eager"
-    log(f"timing {args.steps} steps")
+    log(f"timing {args.steps} steps (each timed loop after {args.settle_ms:g} ms of untimed clock settling)")
+    settle(torch, step, args.settle_ms)
     eager_ms = time_steps(step)
     graph_ms = None
     if not args.eager:
@@ -584,6 +623,7 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
+        settle(torch, graph.replay, args.settle_ms)
         for _ in range(args.warmup):
             graph.replay()
         graph_ms = time_steps(graph.replay)
@@ -593,6 +633,7 @@ def main():
     fused_eager_ms = fused_graph_ms = None
     if fused_ok:
         # the same rows reach the same slots either way, so the caches stay as they were
+        settle(torch, step_fused, args.settle_ms)
         for _ in range(args.warmup):
             step_fused()
         fused_eager_ms = time_steps(step_fused)
@@ -600,6 +641,7 @@ def main():
             graph_f = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph_f):
                 step_fused()
+            settle(torch, graph_f.replay, args.settle_ms)
             for _ in range(args.warmup):
                 graph_f.replay()
             fused_graph_ms = time_steps(graph_f.replay)
@@ -607,6 +649,7 @@ def main():
         append_mode = "fused"
 
     # per-kernel timing of the attention call (the dominant kernel), same stream
+    settle(torch, step, args.settle_ms)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for z, a, b in evs:
@@ -655,7 +698,7 @@ def main():
                           if P > 1 else "fe_paged_gqa_decode (gqa_decode_partition_kernel)",
                 "per_launch_bytes": att_bytes, "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5),
                 **att_spread, "cold_median_ms": round(cold_med_ms, 5)}
-        ceil = streaming_read_ceiling(torch, dev, fe)
+        ceil = streaming_read_ceiling(torch, dev, fe, args.settle_ms)
         roof["streaming_read_ceiling"] = ceil
         roof["frac_of_streaming_ceiling"] = round(achieved / ceil["GBps"], 4)
         metric = "paged GQA decode achieved HBM GB/s (% of peak) + KV tokens/s, Qwen3-4B shape"
@@ -690,7 +733,7 @@ def main():
                 "kernel": "fe_paged_gqa_prefill_chunk (gqa_prefill_chunk_kernel)", "per_launch_flops": flops,
                 "avg_ms": round(att_avg_ms, 5), "median_ms": round(att_med_ms, 5), **att_spread,
                 "cold_median_ms": round(cold_med_ms, 5)}
-        mceil = sustained_mfma_ceiling(torch, dev, fe)
+        mceil = sustained_mfma_ceiling(torch, dev, fe, args.settle_ms)
         roof["sustained_mfma_ceiling"] = mceil
         roof["frac_of_sustained_mfma_ceiling"] = round(achieved / mceil["TFLOPs"], 4)
         metric = "paged GQA chunked-prefill TFLOP/s (% of bf16 MFMA peak), Qwen3-4B shape"
@@ -711,7 +754,7 @@ def main():
     cfg = {"workload": spec.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": 128,
            "block_size": 16, "layers": nl, "kv_tokens": w.kv_tokens, "max_context_len": mcl,
            "append_tokens_per_step": int(slots.numel()) * nl, "num_partitions": P, "seed": w.seed,
-           "launch": launch, "append": append_mode, "eager_ms_per_step": round(eager_ms, 5),
+           "launch": launch, "settle_ms": args.settle_ms, "append": append_mode, "eager_ms_per_step": round(eager_ms, 5),
            "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
            "separate_append_ms_per_step": round(separate_ms, 5) if do_append else None,
            "fused_eager_ms_per_step": None if fused_eager_ms is None else round(fused_eager_ms, 5),
