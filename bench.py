@@ -452,6 +452,19 @@ def bench_sampler(args, fe, inputs, torch, dev):
         fe.fe_sampler_softmax_argmax(probs, lse, am, x, it, workspace=ws)
 
     ms, per, launch, eager_ms, graph_ms = time_calls(args, torch, step)
+    # the automatic form, and each form timed on its own (eager, settled)
+    form = fe.fe_sampler_form(B, V)
+    form_ms = {}
+    for f in (1, 2):
+        call = lambda: fe.fe_sampler_softmax_argmax_ex(probs, lse, am, x, it, f, workspace=ws)
+        settle(torch, call, args.settle_ms)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(torch.cuda.current_stream())
+        for _ in range(args.steps):
+            call()
+        b.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        form_ms[f] = a.elapsed_time(b) / args.steps
     # the achieved rate uses the average launch duration over the timed
     # region of back-to-back launches (ms); per-call events around a call this
     # short also hold host launch gaps and are kept as the spread only
@@ -460,7 +473,8 @@ def bench_sampler(args, fe, inputs, torch, dev):
     achieved = nbytes / (avg * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(f"sampler:qwen3_vocab{V}_b{B}", "sampler", 0),
-            "kernel": "fe_sampler_softmax_argmax (sampler_partial_kernel + sampler_write_kernel)",
+            "kernel": "fe_sampler_softmax_argmax (" + ("sampler_row_kernel" if form == 2 else
+                                                        "sampler_partial_kernel + sampler_write_kernel") + ")",
             "per_launch_bytes": nbytes, "avg_ms": round(avg, 5), "per_call_avg_ms": round(sum(per) / len(per), 5),
             "median_ms": round(per[len(per) // 2], 5), **spread(per)}
     ceil = streaming_read_ceiling(torch, dev, fe, args.settle_ms)
@@ -482,6 +496,8 @@ def bench_sampler(args, fe, inputs, torch, dev):
         cpu = {"value": round(nbytes / (el / reps) / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"fp64 oracle over all {B} rows of {V} logits, {reps} repetitions, {el / reps * 1e3:.1f} ms each"}
     cfg = {"workload": f"sampler:qwen3_vocab{V}_b{B}", "batch": B, "vocab": V, "seed": args.seed or 1,
+           "form": {1: "ranges (two launches)", 2: "one workgroup per row"}[form],
+           "form1_ranges_ms": round(form_ms[1], 5), "form2_row_per_workgroup_ms": round(form_ms[2], 5),
            "launch": launch, "settle_ms": args.settle_ms, "eager_ms_per_step": round(eager_ms, 5),
            "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5)}
     rec = {"metric": "fp32 softmax + argmax over the vocabulary, achieved HBM GB/s", "value":

@@ -368,7 +368,9 @@ size_t fe_sampler_workspace_size(int B, int V);
  *   logits         bf16 [B][V]; V must be a multiple of 8 (FE_ERR_UNSUPPORTED)
  *   inv_temperature  fp32 [B] (> 0, finite; not checked) or NULL
  *   workspace      device scratch of fe_sampler_workspace_size(B, V) bytes,
- *                  clobbered
+ *                  clobbered (required; the one-workgroup-per-row form
+ *                  leaves it untouched)
+ * Runs the form fe_sampler_softmax_argmax_ex picks with form 0.
  * Source: "Make the Engine Talk" section 1.3 (the sampler: greedy,
  * temperature and top-p decoding, with its softmax in fp32 over a vocabulary
  * this wide); ForgeEngine README, "What it implements" (sampling policies).
@@ -376,6 +378,34 @@ size_t fe_sampler_workspace_size(int B, int V);
 int fe_sampler_softmax_argmax(float* probs, float* lse, int32_t* argmax, const void* logits,
                               const float* inv_temperature, int B, int V, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * fe_sampler_softmax_argmax with the kernel form chosen by the caller; the
+ * results are the same up to fp32 summation order.
+ *   form 0  automatic: form 2 when V <= 163,840 and B >= 160 with B mod 256
+ *           either 0 or at least 160 (every round of 256 workgroups, one per
+ *           CU, holds at least 160 rows), else form 1
+ *   form 1  ranges: each row cut into ranges over about 1024 workgroups, a
+ *           pass for the ranges' partials and a pass that merges them and
+ *           writes (two launches; the logits are read twice)
+ *   form 2  one workgroup of 1024 threads per row, the row held in registers
+ *           (one launch, the logits read once; a CU streams one row at a few
+ *           tens of GB/s, so it pays only when the rows cover the CUs);
+ *           FE_ERR_UNSUPPORTED when V > 163,840
+ *   other   FE_ERR_INVALID_ARG
+ * Other arguments and errors as fe_sampler_softmax_argmax.
+ * Source: as fe_sampler_softmax_argmax.
+ */
+int fe_sampler_softmax_argmax_ex(float* probs, float* lse, int32_t* argmax, const void* logits,
+                                 const float* inv_temperature, int B, int V, int form, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The form (1 or 2) that form 0 of fe_sampler_softmax_argmax_ex runs for B
+ * rows of V logits (host-only; -1 for invalid sizes).
+ * Source: as fe_sampler_softmax_argmax.
+ */
+int fe_sampler_form(int B, int V);
 
 /*
  * Paged KV block allocator (host memory, host calls only): hands out the

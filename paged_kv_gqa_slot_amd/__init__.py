@@ -29,7 +29,9 @@ from .binding import (  # noqa: F401
     fe_paged_gqa_prefill_chunk_ex,
     fe_paged_kv_append,
     fe_qk_norm_rope_append,
+    fe_sampler_form,
     fe_sampler_softmax_argmax,
+    fe_sampler_softmax_argmax_ex,
     fe_sampler_workspace_size,
     fe_status_string,
     library_path,

@@ -83,6 +83,10 @@ def load_library():
     lib.fe_sampler_workspace_size.restype = Z
     lib.fe_sampler_softmax_argmax.argtypes = [P, P, P, P, P, I, I, P, Z, P]
     lib.fe_sampler_softmax_argmax.restype = I
+    lib.fe_sampler_softmax_argmax_ex.argtypes = [P, P, P, P, P, I, I, I, P, Z, P]
+    lib.fe_sampler_softmax_argmax_ex.restype = I
+    lib.fe_sampler_form.argtypes = [I, I]
+    lib.fe_sampler_form.restype = I
     lib.fe_hbm_read_probe.argtypes = [P, ctypes.c_int64, P, I, P, P]
     lib.fe_hbm_read_probe.restype = I
     lib.fe_mfma_rate_probe.argtypes = [P, I, I, I, P, P]
@@ -399,8 +403,23 @@ def fe_sampler_workspace_size(B: int, V: int) -> int:
     return int(n)
 
 
+def fe_sampler_form(B: int, V: int) -> int:
+    """The sampler form the automatic choice runs: 1 ranges, 2 one workgroup per row."""
+    f = load_library().fe_sampler_form(int(B), int(V))
+    if f < 0:
+        raise ValueError("fe_sampler_form: invalid sizes")
+    return int(f)
+
+
 def fe_sampler_softmax_argmax(probs, lse, argmax, logits, inv_temperature=None, workspace=None, stream=None) -> None:
     """fp32 softmax (probs may be None), LSE (may be None) and greedy argmax of bf16 logits [B][V]."""
+    fe_sampler_softmax_argmax_ex(probs, lse, argmax, logits, inv_temperature, 0, workspace, stream)
+
+
+def fe_sampler_softmax_argmax_ex(probs, lse, argmax, logits, inv_temperature=None, form: int = 0, workspace=None,
+                                 stream=None) -> None:
+    """fe_sampler_softmax_argmax with the kernel form chosen: 0 automatic, 1
+    ranges (two launches), 2 one workgroup per row (one launch)."""
     _shape(logits, "logits", None, None)
     B, V = logits.shape
     _shape(probs, "probs", B, V)
@@ -410,11 +429,11 @@ def fe_sampler_softmax_argmax(probs, lse, argmax, logits, inv_temperature=None, 
     ws_bytes = fe_sampler_workspace_size(B, V)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=logits.device)
-    rc = load_library().fe_sampler_softmax_argmax(
+    rc = load_library().fe_sampler_softmax_argmax_ex(
         _dev(probs, torch.float32, "probs", 2), _dev(lse, torch.float32, "lse", 1),
         _dev(argmax, torch.int32, "argmax", 1), _dev(logits, torch.bfloat16, "logits", 2),
-        _dev(inv_temperature, torch.float32, "inv_temperature", 1), B, V, _dev(workspace, torch.uint8, "workspace"),
-        workspace.numel(), _stream(stream))
+        _dev(inv_temperature, torch.float32, "inv_temperature", 1), B, V, int(form),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(rc, "fe_sampler_softmax_argmax")
 
 

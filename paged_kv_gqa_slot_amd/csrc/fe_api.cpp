@@ -324,22 +324,36 @@ int fe_qk_norm_rope_append(void* q_out, const void* q, const void* k, const void
 
 size_t fe_sampler_workspace_size(int B, int V) {
   if (B < 0 || V <= 0 || V % 8 != 0) return static_cast<size_t>(-1);
-  return fe::plan_sampler(B, V).workspace_bytes;
+  fe::SamplerPlan plan;
+  fe::plan_sampler(B, V, 0, &plan);  // form 0 always plans; the size is the ranges form's, for every form
+  return plan.workspace_bytes;
 }
 
-int fe_sampler_softmax_argmax(float* probs, float* lse, int32_t* argmax, const void* logits,
-                              const float* inv_temperature, int B, int V, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream) {
+int fe_sampler_form(int B, int V) {
+  if (B < 0 || V <= 0 || V % 8 != 0) return -1;
+  fe::SamplerPlan plan;
+  fe::plan_sampler(B, V, 0, &plan);
+  return plan.row_per_workgroup ? 2 : 1;
+}
+
+int fe_sampler_softmax_argmax_ex(float* probs, float* lse, int32_t* argmax, const void* logits,
+                                 const float* inv_temperature, int B, int V, int form, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
   static const char* fn = "fe_sampler_softmax_argmax";
   try {
     if (B < 0 || V <= 0) return fail(FE_ERR_INVALID_ARG, fn, "B must be >= 0 and V positive");
+    if (form < 0 || form > 2) return fail(FE_ERR_INVALID_ARG, fn, "form must be 0, 1 or 2");
     if (V % 8 != 0) return fail(FE_ERR_UNSUPPORTED, fn, "V must be a multiple of 8");
     if (B == 0) return FE_OK;
     if (!argmax || !logits) return fail(FE_ERR_NULL, fn, "argmax and logits must not be NULL");
     if (!aligned16(logits) || !aligned16(probs))
       return fail(FE_ERR_INVALID_ARG, fn, "logits and probs must be 16-byte aligned");
-    const fe::SamplerPlan plan = fe::plan_sampler(B, V);
-    if (!launch_fits(static_cast<double>(B) * plan.chunks, 256)) return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
+    fe::SamplerPlan plan;
+    if (!fe::plan_sampler(B, V, form, &plan))
+      return fail(FE_ERR_UNSUPPORTED, fn, "form 2 (one workgroup per row) holds rows of at most 163,840 logits");
+    if (!launch_fits(plan.row_per_workgroup ? static_cast<double>(B) : static_cast<double>(B) * plan.chunks,
+                     plan.row_per_workgroup ? fe::kSamplerRowThreads : 256))
+      return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     if (!workspace || workspace_bytes < plan.workspace_bytes)
       return fail(FE_ERR_WORKSPACE, fn, "workspace missing or smaller than fe_sampler_workspace_size()");
     const fe::SamplerArgs a{probs, lse, argmax, logits, inv_temperature, B, V, plan, workspace};
@@ -348,6 +362,13 @@ int fe_sampler_softmax_argmax(float* probs, float* lse, int32_t* argmax, const v
   } catch (...) {
     return fail(FE_ERR_INTERNAL, fn, "unexpected exception");
   }
+}
+
+int fe_sampler_softmax_argmax(float* probs, float* lse, int32_t* argmax, const void* logits,
+                              const float* inv_temperature, int B, int V, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  return fe_sampler_softmax_argmax_ex(probs, lse, argmax, logits, inv_temperature, B, V, 0, workspace,
+                                      workspace_bytes, stream);
 }
 
 int fe_hbm_read_probe(const void* base, int64_t num_tiles, const int32_t* tile_ids, int n, uint32_t* sink,

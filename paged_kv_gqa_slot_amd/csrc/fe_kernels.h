@@ -117,18 +117,34 @@ struct NormRopeArgs {
   float eps;
 };
 
-// Sampler plan: each row of V logits is cut into `chunks` ranges of
-// `chunk_units` 8-logit units; the workspace holds one 16-byte partial per
-// (row, range).
+// Sampler plan.  Two forms:
+//  * ranges (two launches): each row of V logits is cut into `chunks` ranges
+//    of `chunk_units` 8-logit units; the workspace holds one 16-byte partial
+//    per (row, range);
+//  * one workgroup per row (one launch): the row stays in the registers of
+//    kSamplerRowThreads threads, at most kSamplerRowUnits units each, and is
+//    read once.  One CU moves a row at only a few tens of GB/s, and one such
+//    workgroup fills a CU, so this form needs rows that cover the CUs: the
+//    automatic choice takes it when every round of kSamplerRowRound
+//    workgroups (one per CU) holds at least kSamplerRowMinBatch rows.
+// workspace_bytes is the ranges form's size whichever form runs, so that a
+// workspace sized by the query serves either.
 struct SamplerPlan {
   int chunks;
   int chunk_units;
   size_t workspace_bytes;
+  bool row_per_workgroup;
 };
 constexpr int kSamplerTargetWgs = 1024;  // about 4 workgroups per CU
 constexpr int kSamplerMinUnits = 512;    // ranges of at least 4096 logits
 constexpr int kSamplerMaxUnits = 2048;   // ... and at most 16384 (8 units per thread)
-SamplerPlan plan_sampler(int B, int V);
+constexpr int kSamplerRowThreads = 1024;
+constexpr int kSamplerRowUnits = 20;     // rows of up to 163,840 logits
+constexpr int kSamplerRowMinBatch = 160;
+constexpr int kSamplerRowRound = 256;
+// form: 0 automatic, 1 ranges, 2 one workgroup per row.  Returns false for a
+// form this V cannot take (2 with V beyond the registers' reach).
+bool plan_sampler(int B, int V, int form, SamplerPlan* plan);
 
 struct SamplerArgs {
   float* probs;

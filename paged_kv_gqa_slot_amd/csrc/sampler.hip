@@ -12,6 +12,10 @@
 // partials (a few dozen bytes, one load per lane), then write the range's
 // probabilities; range 0 also writes the argmax and the LSE.  Each thread reads 8 bf16 logits per
 // 16-byte load.
+//
+// With enough rows to cover the CUs, one workgroup of 1024 threads per row
+// instead: the row stays in registers, so the logits are read once and one
+// launch does both passes, with the row's merge in LDS.
 #include <math.h>
 
 #include "fe_device.h"
@@ -219,14 +223,93 @@ __global__ __launch_bounds__(kThreads) void sampler_write_kernel(SamplerParams p
   }
 }
 
+// One workgroup per row: every thread issues all of its loads (units
+// clamped into the row; those past it are not used), folds them into an
+// online (max, sum, first maximum) as pass 1 does, the 16 waves' results
+// merge through LDS, and the probabilities are written from the registers.
+constexpr int kRowWaves = kSamplerRowThreads / 64;
+
+__global__ __launch_bounds__(kSamplerRowThreads) void sampler_row_kernel(SamplerParams p) {
+  const int b = blockIdx.x;
+  const float sc = row_scale(p, b);
+  const int units = p.V / 8;
+  const uint4* row = reinterpret_cast<const uint4*>(p.logits + static_cast<size_t>(b) * p.V);
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t w[kSamplerRowUnits];
+  const int last = units - 1;
+#pragma unroll
+  for (int k = 0; k < kSamplerRowUnits; ++k) {
+    const int u = min(static_cast<int>(threadIdx.x) + k * kSamplerRowThreads, last);
+    w[k] = *reinterpret_cast<const u32x4_t*>(&row[u]);
+  }
+  float m = -INFINITY, sum = 0.f, best_v = -INFINITY;
+  int best_i = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < kSamplerRowUnits; ++k) {
+    const int u = threadIdx.x + k * kSamplerRowThreads;
+    if (u >= units) break;
+    const float x[8] = {bf16_lo(w[k][0]), bf16_hi(w[k][0]), bf16_lo(w[k][1]), bf16_hi(w[k][1]),
+                        bf16_lo(w[k][2]), bf16_hi(w[k][2]), bf16_lo(w[k][3]), bf16_hi(w[k][3])};
+    float um = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      um = fmaxf(um, x[j] * sc);
+      if (x[j] > best_v) {  // indices grow along a thread's walk: the first maximum stays
+        best_v = x[j];
+        best_i = 8 * u + j;
+      }
+    }
+    const float M = fmaxf(m, um);
+    if (M == -INFINITY) continue;  // everything so far is masked
+    float t = m == -INFINITY ? 0.f : sum * fast_exp2(m - M);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += fast_exp2(x[j] * sc - M);
+    m = M;
+    sum = t;
+  }
+  wave_merge(m, sum, best_v, best_i);
+  __shared__ Partial sh[kRowWaves];
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) sh[threadIdx.x >> 6] = Partial{m, sum, best_v, best_i};
+  __syncthreads();
+  // every wave merges the 16 partials (lanes past them hold empty ones, which
+  // merge as nothing)
+  Partial q = lane < kRowWaves ? sh[lane] : Partial{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+  wave_merge(q.m, q.sum, q.best_v, q.best_i);
+  const bool empty = q.m == -INFINITY;
+  if (threadIdx.x == 0) {
+    p.argmax[b] = empty ? 0 : q.best_i;
+    if (p.lse) p.lse[b] = empty ? -INFINITY : (q.m + log2f(q.sum)) * kLn2;
+  }
+  if (!p.probs) return;
+  const float invZ = empty ? 0.f : 1.0f / q.sum;
+  float4* out = reinterpret_cast<float4*>(p.probs + static_cast<size_t>(b) * p.V);
+#pragma unroll
+  for (int k = 0; k < kSamplerRowUnits; ++k) {
+    const int u = threadIdx.x + k * kSamplerRowThreads;
+    if (u >= units) break;
+    const float x[8] = {bf16_lo(w[k][0]), bf16_hi(w[k][0]), bf16_lo(w[k][1]), bf16_hi(w[k][1]),
+                        bf16_lo(w[k][2]), bf16_hi(w[k][2]), bf16_lo(w[k][3]), bf16_hi(w[k][3])};
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = empty ? 0.f : fast_exp2(x[j] * sc - q.m) * invZ;
+    const f32x4_t lo = {e[0], e[1], e[2], e[3]}, hi = {e[4], e[5], e[6], e[7]};
+    *reinterpret_cast<f32x4_t*>(&out[2 * u]) = lo;
+    *reinterpret_cast<f32x4_t*>(&out[2 * u + 1]) = hi;
+  }
+}
+
 }  // namespace
 
-SamplerPlan plan_sampler(int B, int V) {
-  SamplerPlan r{1, 0, 0};
-  if (B <= 0 || V <= 0) return r;
+bool plan_sampler(int B, int V, int form, SamplerPlan* plan) {
+  SamplerPlan r{1, 0, 0, false};
+  *plan = r;
+  if (B <= 0 || V <= 0) return true;
   const int units = V / 8;
-  // about 4 workgroups per CU over the batch, ranges of at least 512 units,
-  // and never more than kSamplerMaxUnits units (what the threads load at once)
+  // ranges: about 4 workgroups per CU over the batch, ranges of at least 512
+  // units, and never more than kSamplerMaxUnits units (what the threads load
+  // at once)
   int chunks = (kSamplerTargetWgs + B - 1) / B;
   const int max_chunks = (units + kSamplerMinUnits - 1) / kSamplerMinUnits;
   if (chunks > max_chunks) chunks = max_chunks;
@@ -236,7 +319,16 @@ SamplerPlan plan_sampler(int B, int V) {
   r.chunks = chunks;
   r.chunk_units = (units + chunks - 1) / chunks;
   r.workspace_bytes = static_cast<size_t>(B) * chunks * sizeof(Partial);
-  return r;
+  const bool row_fits = units <= kSamplerRowThreads * kSamplerRowUnits;
+  if (form == 2 && !row_fits) return false;
+  // automatic: rows in the last round of workgroups (one per CU); a round
+  // with fewer than kSamplerRowMinBatch rows leaves most CUs idle through a
+  // row's whole time
+  const int last_round = B % kSamplerRowRound == 0 ? kSamplerRowRound : B % kSamplerRowRound;
+  const bool row_pays = B >= kSamplerRowMinBatch && last_round >= kSamplerRowMinBatch;
+  r.row_per_workgroup = form == 2 || (form == 0 && row_fits && row_pays);
+  *plan = r;
+  return true;
 }
 
 hipError_t launch_sampler(const SamplerArgs& a, hipStream_t stream) {
@@ -251,9 +343,14 @@ hipError_t launch_sampler(const SamplerArgs& a, hipStream_t stream) {
   p.V = a.V;
   p.chunks = a.plan.chunks;
   p.chunk_units = a.plan.chunk_units;
+  void* args[] = {&p};
+  if (a.plan.row_per_workgroup) {
+    if (a.B == 0) return hipSuccess;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&sampler_row_kernel), dim3(static_cast<unsigned>(a.B)),
+                           dim3(kSamplerRowThreads), args, 0, stream);
+  }
   const unsigned grid = static_cast<unsigned>(static_cast<long>(a.B) * p.chunks);
   if (grid == 0) return hipSuccess;
-  void* args[] = {&p};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sampler_partial_kernel), dim3(grid), dim3(kThreads),
                                  args, 0, stream);
   if (e != hipSuccess) return e;

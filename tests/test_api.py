@@ -311,6 +311,40 @@ def test_sampler_argument_errors(lib):
     assert lib.fe_sampler_workspace_size(4, 1001) == ctypes.c_size_t(-1).value
 
 
+def smp_ex(lib, form, **kw):
+    a = dict(probs=P, lse=P, am=P, x=P, it=None, B=4, V=1024, ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.fe_sampler_softmax_argmax_ex(a["probs"], a["lse"], a["am"], a["x"], a["it"], a["B"], a["V"], form,
+                                            a["ws"], a["wsb"], a["stream"])
+
+
+def test_sampler_form_argument_errors(lib):
+    """form must be 0, 1 or 2; the one-workgroup-per-row form holds rows of
+    at most 1024 threads x 20 units x 8 logits; every form needs the
+    workspace the size query gives."""
+    assert smp_ex(lib, 3) == INVALID and "form" in fe.fe_last_error()
+    assert smp_ex(lib, -1) == INVALID
+    assert smp_ex(lib, 2, V=163840 + 8) == UNSUPPORTED and "163,840" in fe.fe_last_error()
+    assert smp_ex(lib, 2, ws=None) == WORKSPACE
+    assert smp_ex(lib, 0, B=256, V=151936, ws=None) == WORKSPACE
+    assert smp_ex(lib, 2, B=0, x=None, am=None) == OK
+    assert smp_ex(lib, 1, V=1001) == UNSUPPORTED
+
+
+def test_sampler_automatic_form():
+    """One workgroup per row (form 2) once every round of 256 workgroups holds
+    at least 160 rows and the row fits 1024 threads x 20 units; ranges (form
+    1) otherwise."""
+    V = 151936
+    assert [fe.fe_sampler_form(B, V) for B in (1, 64, 128, 159)] == [1, 1, 1, 1]
+    assert [fe.fe_sampler_form(B, V) for B in (160, 192, 256, 512, 1024, 416)] == [2, 2, 2, 2, 2, 2]
+    assert [fe.fe_sampler_form(B, V) for B in (300, 384, 512 + 159)] == [1, 1, 1]
+    assert fe.fe_sampler_form(256, 163840) == 2 and fe.fe_sampler_form(256, 163848) == 1
+    assert fe.fe_sampler_form(0, V) == 1
+    with pytest.raises(ValueError):
+        fe.fe_sampler_form(4, 1001)
+
+
 def test_oversized_launches_rejected(lib):
     """Sizes whose launch would reach 2^32 work-items are refused on the host."""
     assert app(lib, T=1 << 30, NB=1 << 20) == UNSUPPORTED
