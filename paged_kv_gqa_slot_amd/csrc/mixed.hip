@@ -8,7 +8,8 @@
 // query_start_loc[b]); sequences [num_decode, B) are prefill chunks.  One
 // grid holds both kinds of workgroup: first the decode items (sequence, KV
 // head, partition), run by as many waves as a prefill tile, then the prefill
-// query tiles (query tile slowest, for the XCD-aware order).  A split decode
+// query tiles, in groups of 8 (sequence, KV head) pairs (one per XCD) with a
+// group's query tiles next to each other.  A split decode
 // sequence is merged in the same launch by the last of its partitions to
 // finish.  Every workgroup reserves the prefill tile's LDS and registers, so
 // a CU runs one workgroup of either kind at a time; the two kinds overlap

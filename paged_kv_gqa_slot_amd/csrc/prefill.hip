@@ -51,12 +51,14 @@ hipError_t launch_shape(PrefillParams prm, long grid, hipStream_t stream) {
 
 // Key groups per workgroup.  Two groups (8 waves, one workgroup per CU) pair
 // each SIMD's MFMA phase with the other group's softmax phase; with at most
-// one workgroup per CU that is the faster shape.  A larger grid runs
-// workgroups back to back on each CU, and there one group per workgroup
-// (two resident workgroups per CU) wins: one workgroup's prologue, epilogue
-// and tail overlap the other's key loop.  Measured on MI355X at Hq/Hkv = 4:
-// 256 workgroups, two groups 12% faster; 384 to 512, one group 2-5% faster;
-// 768 to 4096, one group 12-15% faster.
+// one workgroup per CU, splitting a tile's keys between them is the faster
+// shape.  A larger grid runs workgroups back to back on each CU, where a
+// split key loop pays its prologue and merge per half.  There one group per
+// workgroup (two resident per CU, overlapping one workgroup's prologue and
+// tail with the other's loop) beat the split by 12-15% at 768 to 4096
+// workgroups, and two query tiles per workgroup over one K/V stream (groups
+// of 4 waves) beat one group: 394 against 476 us on 64 x (1024 + 256),
+// keeping the ping-pong and reading each pair of tiles' K/V once.
 template <int G>
 hipError_t launch_g(const PrefillArgs& a, const PrefillParams& prm, hipStream_t stream) {
   PrefillParams copy = prm;
