@@ -214,11 +214,11 @@ def time_separate_calls(fe, torch, w, x, nd, qsl, bt, lens, mcl, steps, stream, 
 
 
 KERNEL_SOURCES = {
-    "norm_rope": ["qk_norm_rope.hip", "fe_device.h"],
+    "norm_rope": ["qk_norm_rope.hip", "norm_rope_row.h", "fe_device.h"],
     "sampler": ["sampler.hip", "fe_device.h"],
-    "decode": ["decode.hip", "decode_body.h", "fe_device.h"],
+    "decode": ["decode.hip", "decode_body.h", "norm_rope_row.h", "fe_device.h"],
     "prefill": ["prefill.hip", "prefill_body.h", "fe_device.h"],
-    "mixed": ["mixed.hip", "decode_body.h", "prefill_body.h", "fe_device.h"],
+    "mixed": ["mixed.hip", "decode_body.h", "norm_rope_row.h", "prefill_body.h", "fe_device.h"],
 }
 
 
@@ -438,6 +438,59 @@ def bench_norm_rope(args, w, fe, inputs, torch, dev):
     print(json.dumps(rec), flush=True)
 
 
+def bench_decode_norm_rope(args, w, fe, inputs, torch, dev):
+    """The whole per-token attention step of a decode workload (one new
+    token per sequence): per-head QK-RMSNorm + rotary of q and the new k, the
+    append, and decode -- as one fe_paged_gqa_decode_norm_rope_append launch,
+    against fe_qk_norm_rope_append followed by fe_paged_gqa_decode."""
+    assert w.spec.kind == "decode" and int(w.slot_mapping.numel()) == w.B, "a decode workload with one new token each"
+    c = inputs.norm_rope_case(w, w.seed, max_pos=max(w.max_context_len, 1))
+    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+    qw, kw, cs = c.q_norm_w.to(dev), c.k_norm_w.to(dev), c.cos_sin.to(dev)
+    pos, sm = c.positions.to(dev), c.slot_mapping.to(dev)
+    kc, vc = c.k_cache.to(dev), c.v_cache.to(dev)
+    bt, lens = w.block_tables.to(dev), w.context_lens.to(dev)
+    mcl = w.max_context_len
+    out = torch.empty(w.B, w.Hq, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.B, w.Hq, dtype=torch.float32, device=dev)
+    q_out = torch.empty_like(q)
+    ws = torch.empty(max(fe.fe_paged_gqa_decode_workspace_size(w.B, w.Hq, w.Hkv, 128, mcl, args.partitions), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def fused():
+        fe.fe_paged_gqa_decode_norm_rope_append(out, lse, q, k, v, qw, kw, cs, pos, sm, kc, vc, bt, lens, mcl,
+                                                w.scale, c.eps, num_partitions=args.partitions, workspace=ws)
+
+    def two_calls():
+        fe.fe_qk_norm_rope_append(q_out, q, k, v, qw, kw, cs, pos, sm, kc, vc, c.eps)
+        fe.fe_paged_gqa_decode(out, lse, q_out, kc, vc, bt, lens, mcl, w.scale, num_partitions=args.partitions,
+                               workspace=ws)
+
+    # the same rows reach the same slots every step, so the pools stay as they are
+    ms, per, launch, eager_ms, graph_ms = time_calls(args, torch, fused)
+    _, _, _, two_eager_ms, two_graph_ms = time_calls(args, torch, two_calls)
+    T = w.B
+    nbytes = decode_bytes(w) + append_bytes(w) + T * (128 * 4 + 4) + 2 * 128 * 2  # + table rows, positions, weights
+    roof = {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "fe_paged_gqa_decode_norm_rope_append (gqa_decode_partition_kernel + gqa_decode_merge_kernel)",
+            "per_launch_bytes": nbytes, "avg_ms": round(ms, 5), "per_call_avg_ms": round(sum(per) / len(per), 5),
+            "median_ms": round(per[len(per) // 2], 5), **spread(per)}
+    cfg = {"workload": f"decode_norm_rope:{w.spec.name}", "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+           "head_dim": 128, "block_size": 16, "max_context_len": mcl, "seed": w.seed, "launch": launch,
+           "settle_ms": args.settle_ms, "eager_ms_per_step": round(eager_ms, 5),
+           "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+           "two_calls_eager_ms_per_step": round(two_eager_ms, 5),
+           "two_calls_graph_ms_per_step": None if two_graph_ms is None else round(two_graph_ms, 5)}
+    rec = {"metric": "per-token attention step (QK-RMSNorm + rotary + append + paged GQA decode) in one launch, "
+                     "achieved HBM GB/s, Qwen3-4B shape",
+           "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg, "roofline": roof,
+           "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def bench_sampler(args, fe, inputs, torch, dev):
     """fp32 softmax + LSE + greedy argmax over the Qwen3 vocabulary for a batch of rows."""
     B, V = args.sampler_batch, inputs.QWEN3_VOCAB
@@ -523,8 +576,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from the host each step instead of replaying a captured HIP graph")
-    ap.add_argument("--op", choices=["attention", "norm_rope", "sampler"], default="attention",
+    ap.add_argument("--op", choices=["attention", "norm_rope", "decode_norm_rope", "sampler"], default="attention",
                     help="norm_rope: the fused QK-RMSNorm + rotary + append step on the workload's new tokens; "
+                         "decode_norm_rope: that step and decode in one launch (decode workloads); "
                          "sampler: fp32 softmax + argmax over the Qwen3 vocabulary for --sampler-batch rows")
     ap.add_argument("--sampler-batch", type=int, default=64)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -552,6 +606,8 @@ def main():
 
     if args.op == "norm_rope":
         return bench_norm_rope(args, w, fe, inputs, torch, dev)
+    if args.op == "decode_norm_rope":
+        return bench_decode_norm_rope(args, w, fe, inputs, torch, dev)
 
     L = [dict(kc=l.k_cache.to(dev), vc=l.v_cache.to(dev), q=l.q.to(dev), kn=l.k_new.to(dev), vn=l.v_new.to(dev))
          for l in w.layers]

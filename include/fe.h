@@ -214,6 +214,42 @@ int fe_paged_gqa_decode_append(void* out, float* lse, const void* q, const void*
                                hipStream_t stream);
 
 /*
+ * The whole per-token attention step of a layer in one launch: the
+ * per-head QK-RMSNorm + rotary embedding of fe_qk_norm_rope_append applied to
+ * q and to the new k rows, the append of the new K/V rows, and decode.
+ *   q             bf16 [B][Hq][D]: the projected (not yet normalised) queries
+ *   k_new, v_new  bf16 [B][Hkv][D]: the projected new K and V rows
+ *   q_norm_w, k_norm_w, cos_sin, max_pos, positions (int32 [B]), eps: as in
+ *                 fe_qk_norm_rope_append (positions[b] is usually
+ *                 context_lens[b] - 1)
+ *   slot_mapping  int32 [B], with the preconditions of
+ *                 fe_paged_gqa_decode_append
+ *   every other argument as fe_paged_gqa_decode_append (same workspace size)
+ * The result equals fe_qk_norm_rope_append(q_out, q, k_new, v_new, ...,
+ * slot_mapping, k_cache, v_cache, T = B) followed by fe_paged_gqa_decode on
+ * q_out (the same normalisation and rotation arithmetic, rounded to bf16 at
+ * the same point), with no q_out written: each workgroup normalises and
+ * rotates the q rows of its KV head itself, and the workgroup that holds b's
+ * last block does the same to the new k row before it writes and attends to
+ * it.  Errors as fe_paged_gqa_decode_append, plus FE_ERR_INVALID_ARG for
+ * max_pos <= 0, an eps that is negative or not finite, or norm weights or
+ * cos_sin not 16-byte aligned, and FE_ERR_NULL for a NULL q_norm_w, k_norm_w,
+ * cos_sin or positions when B > 0.
+ * Source: "Make the Engine Talk" sections 1.2-1.3 (each generated token
+ * extends the cache and is attended to, after RMSNorm and rotary embedding);
+ * ForgeEngine README, "What it implements" (RMSNorm kernel, paged KV cache,
+ * CUDA paged GQA kernel).
+ */
+int fe_paged_gqa_decode_norm_rope_append(void* out, float* lse, const void* q, const void* k_new, const void* v_new,
+                                         const void* q_norm_w, const void* k_norm_w, const float* cos_sin,
+                                         int max_pos, const int32_t* positions, const int32_t* slot_mapping,
+                                         void* k_cache, void* v_cache, const int32_t* block_tables,
+                                         int max_blocks_per_seq, const int32_t* context_lens, int B, int Hq, int Hkv,
+                                         int D, int BS, int num_blocks, int max_context_len, float scale, float eps,
+                                         int num_partitions, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
  * Paged GQA prefill of a causal query chunk against the cached prefix.
  *   q              bf16 [total_q][Hq][D], sequences packed back to back
  *   query_start_loc  int32 [B + 1] DEVICE array; sequence b owns packed rows

@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     fe_paged_gqa_decode,
     fe_paged_gqa_decode_append,
     fe_paged_gqa_decode_noalloc,
+    fe_paged_gqa_decode_norm_rope_append,
     fe_paged_gqa_decode_num_partitions,
     fe_paged_gqa_decode_workspace_size,
     fe_paged_gqa_mixed,

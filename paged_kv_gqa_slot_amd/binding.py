@@ -54,6 +54,9 @@ def load_library():
     lib.fe_paged_gqa_decode_noalloc.restype = I
     lib.fe_paged_gqa_decode_append.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, Z, P]
     lib.fe_paged_gqa_decode_append.restype = I
+    lib.fe_paged_gqa_decode_norm_rope_append.argtypes = [P, P, P, P, P, P, P, P, I, P, P, P, P, P, I, P, I, I, I, I,
+                                                         I, I, I, F, F, I, P, Z, P]
+    lib.fe_paged_gqa_decode_norm_rope_append.restype = I
     lib.fe_paged_gqa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, P]
     lib.fe_paged_gqa_prefill_chunk.restype = I
     lib.fe_paged_gqa_prefill_chunk_ex.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, I, P]
@@ -302,6 +305,46 @@ def fe_paged_gqa_decode_append(out, lse, q, k_new, v_new, slot_mapping, k_cache,
         block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens", 1), B, Hq, Hkv, D, BS, NB,
         int(max_context_len), float(scale), int(num_partitions), ws_ptr, ws_have, _stream(stream))
     _check(rc, "fe_paged_gqa_decode_append")
+
+
+def fe_paged_gqa_decode_norm_rope_append(out, lse, q, k_new, v_new, q_norm_w, k_norm_w, cos_sin, positions,
+                                         slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len: int, scale: float, eps: float, num_partitions: int = 0,
+                                         workspace=None, stream=None, validate: bool = False) -> None:
+    """Per-head RMSNorm + rotary embedding of q and of the new k rows, the
+    append of the new K/V rows and decode, in one launch: the same result as
+    fe_qk_norm_rope_append followed by fe_paged_gqa_decode on its q_out.
+    Same workspace as fe_paged_gqa_decode; one is allocated when not given.
+    validate=True checks slot_mapping on host copies as
+    fe_paged_gqa_decode_append does."""
+    _shape(q, "q", None, None, None)
+    B, Hq, D = q.shape
+    NB, Hkv, BS, _ = _pools(k_cache, v_cache)
+    _decode_shapes(out, lse, q, k_cache, block_tables, context_lens)
+    _shape(k_new, "k_new", B, Hkv, D)
+    _shape(v_new, "v_new", B, Hkv, D)
+    _shape(slot_mapping, "slot_mapping", B)
+    _shape(positions, "positions", B)
+    _shape(cos_sin, "cos_sin", None, D)
+    _shape(q_norm_w, "q_norm_w", D)
+    _shape(k_norm_w, "k_norm_w", D)
+    if validate:
+        check_decode_append_slots(slot_mapping, block_tables, context_lens, NB, BS, max_context_len)
+    ws_bytes = fe_paged_gqa_decode_workspace_size(B, Hq, Hkv, D, max_context_len, num_partitions)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, torch.uint8, "workspace") if workspace is not None else None
+    ws_have = workspace.numel() if workspace is not None else 0
+    rc = load_library().fe_paged_gqa_decode_norm_rope_append(
+        _dev(out, torch.bfloat16, "out", 3), _dev(lse, torch.float32, "lse", 2), _dev(q, torch.bfloat16, "q", 3),
+        _dev(k_new, torch.bfloat16, "k_new", 3), _dev(v_new, torch.bfloat16, "v_new", 3),
+        _dev(q_norm_w, torch.bfloat16, "q_norm_w", 1), _dev(k_norm_w, torch.bfloat16, "k_norm_w", 1),
+        _dev(cos_sin, torch.float32, "cos_sin", 2), cos_sin.shape[0], _dev(positions, torch.int32, "positions", 1),
+        _dev(slot_mapping, torch.int32, "slot_mapping", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
+        _dev(v_cache, torch.bfloat16, "v_cache", 4), _dev(block_tables, torch.int32, "block_tables", 2),
+        block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens", 1), B, Hq, Hkv, D, BS, NB,
+        int(max_context_len), float(scale), float(eps), int(num_partitions), ws_ptr, ws_have, _stream(stream))
+    _check(rc, "fe_paged_gqa_decode_norm_rope_append")
 
 
 def _packed_shapes(out, lse, q, query_start_loc, k_cache, block_tables, B):

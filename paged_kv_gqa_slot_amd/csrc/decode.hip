@@ -41,8 +41,9 @@ constexpr int kAutoMinParts = 8;
 constexpr int kAutoFillWgs = 2 * kCuCount;
 constexpr int kAutoMinPartBlocks = 16;
 
-// Pass 1, one workgroup per item (grid B * P * Hkv, Hkv fastest).
-template <int G>
+// Pass 1, one workgroup per item (grid B * P * Hkv, Hkv fastest); kNormRope:
+// the fused per-head RMSNorm + rotary of q and the new k rows.
+template <int G, bool kNormRope>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 2))) void gqa_decode_partition_kernel(
     DecodeParams p) {
   __shared__ DecodeShared<G, kWaves> sh;
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4
   const int g = wg % p.Hkv;
   wg /= p.Hkv;
   const int part = wg % p.P;
-  decode_item<G, kWaves, false>(p, sh, wg / p.P, g, part);
+  decode_item<G, kWaves, false, kNormRope>(p, sh, wg / p.P, g, part);
 }
 
 // Pass 2: one wave per (sequence, query head); lane k owns dims 2k, 2k + 1.
@@ -111,8 +112,9 @@ hipError_t launch_g(const DecodeParams& prm, hipStream_t stream) {
   const long items = static_cast<long>(prm.B) * prm.P * prm.Hkv;
   DecodeParams copy = prm;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gqa_decode_partition_kernel<G>),
-                         dim3(static_cast<unsigned>(items)), dim3(kThreads), args, 0, stream);
+  const void* kernel = prm.q_norm_w ? reinterpret_cast<const void*>(&gqa_decode_partition_kernel<G, true>)
+                                    : reinterpret_cast<const void*>(&gqa_decode_partition_kernel<G, false>);
+  return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(items)), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace
@@ -198,6 +200,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     prm.k_cache_w = static_cast<uint16_t*>(const_cast<void*>(a.k_cache));
     prm.v_cache_w = static_cast<uint16_t*>(const_cast<void*>(a.v_cache));
     prm.num_slots = static_cast<int64_t>(a.num_blocks) * kBlockSize;
+    if (a.q_norm_w) {
+      prm.q_norm_w = static_cast<const uint16_t*>(a.q_norm_w);
+      prm.k_norm_w = static_cast<const uint16_t*>(a.k_norm_w);
+      prm.cos_sin = a.cos_sin;
+      prm.positions = a.positions;
+      prm.max_pos = a.max_pos;
+      prm.eps = a.eps;
+    }
   }
   if (prm.P > 1) {
     prm.o_part = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + a.plan.o_part_offset);

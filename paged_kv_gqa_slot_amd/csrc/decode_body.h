@@ -22,7 +22,9 @@
 //   enter the numerator are the ones summed into l.  A partially filled last block is handled after the main
 //   loop by a masked variant of the same step; with a fused append the last
 //   block always goes that way, and there the new token's row is written to
-//   the cache and patched into the loaded tile.
+//   the cache and patched into the loaded tile.  That form can also
+//   normalise and rotate q and the new k row first (norm_rope_row.h), which
+//   takes the whole per-token attention input step into one launch.
 //
 // At the end the 4 rows and W waves are merged (max-shifted sums) through
 // cross-lane shuffles and LDS.  An unsplit sequence gets its bf16 output and
@@ -35,6 +37,7 @@
 
 #include "fe_device.h"
 #include "fe_kernels.h"
+#include "norm_rope_row.h"
 
 namespace fe {
 namespace dec {
@@ -71,6 +74,16 @@ struct DecodeParams {
   uint16_t* k_cache_w;  // the pools again, writable (fused append only)
   uint16_t* v_cache_w;
   int64_t num_slots;
+  // Fused per-head RMSNorm + rotary of q and of the appended k (the
+  // kNormRope instance of decode_item; only with a fused append): weights
+  // [D] bf16, table [max_pos][D] fp32 at row positions[b], clamped into
+  // [0, max_pos)
+  const uint16_t* q_norm_w;
+  const uint16_t* k_norm_w;
+  const float* cos_sin;
+  const int32_t* positions;
+  int max_pos;
+  float eps;
   int max_blocks, B, Hq, Hkv, num_blocks, ctx_cap;
   int P, part_blocks;
   float scale_log2;  // |scale| * log2(e)
@@ -221,7 +234,7 @@ struct DecodeShared {
 // Without kFused, a split sequence's partitions leave fp32 partials for a
 // separate merge pass.  With kFused, each partition counts its arrival and
 // the last one of the (sequence, KV head) to arrive merges them in place.
-template <int G, int W, bool kFused>
+template <int G, int W, bool kFused, bool kNormRope = false>
 __device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<G, W>& sh, int b, int g, int part) {
   constexpr int kThreads = 64 * W;
   const int tid = threadIdx.x;
@@ -242,11 +255,16 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<
   const int qrow = p.q_rows ? min(max(p.q_rows[b], 0), p.q_rows_count - 1) : b;
   const size_t qrow0 = static_cast<size_t>(qrow) * p.Hq + static_cast<size_t>(g) * G;
   uint32_t qw[G][4];
+  // fused norm/rotary: the position arrives with q; the table row and the
+  // weights are loaded once the tile loads can be issued, and q is
+  // normalised and rotated after them, so neither adds a round trip
+  int nr_pos = 0;
+  if constexpr (kNormRope) nr_pos = p.positions[b];
   {
     const uint4* qp = reinterpret_cast<const uint4*>(p.q + qrow0 * kHeadDim) + c;
 #pragma unroll
     for (int h = 0; h < G; ++h) words4(qp[h * (kHeadDim / 8)], qw[h]);
-    if (p.negate_q) {  // scale < 0: flip q's signs (exact) and use |scale|
+    if (p.negate_q && !kNormRope) {  // scale < 0: flip q's signs (exact) and use |scale|
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -303,9 +321,24 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<
     const int bytes = ok ? kTileElems * 2 : 0;
     load_tile(dst, tile_rsrc(kg + o, bytes), tile_rsrc(vg + o, bytes), lane);
   };
+  RopeLane q_cs;
+  uint4 q_ww;
+  if constexpr (kNormRope) {
+    q_cs = rope_lane(p.cos_sin, min(max(nr_pos, 0), p.max_pos - 1), c);
+    q_ww = reinterpret_cast<const uint4*>(p.q_norm_w)[c];
+  }
   Tile ring[kPrefetch + 1];
 #pragma unroll
   for (int k = 0; k < kPrefetch; ++k) issue(ring[k], k);
+  if constexpr (kNormRope) {  // per-head RMSNorm + rotary of q, as the fused norm/rotary/append call computes it
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      words4(norm_rope_row(make_uint4(qw[h][0], qw[h][1], qw[h][2], qw[h][3]), q_ww, q_cs, p.eps, c), qw[h]);
+      if (p.negate_q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qw[h][i] ^= 0x80008000u;
+    }
+  }
   for (int t = 0; t < n; t += kPrefetch + 1) {
 #pragma unroll
     for (int k = 0; k <= kPrefetch; ++k) {
@@ -325,8 +358,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, DecodeShared<
       // load above may or may not have seen the store.
       const int64_t slot = p.new_slots[b];
       const size_t nrow = (static_cast<size_t>(b) * p.Hkv + g) * kHeadDim;
-      const uint4 kn = reinterpret_cast<const uint4*>(p.k_new + nrow)[c];
+      uint4 kn = reinterpret_cast<const uint4*>(p.k_new + nrow)[c];
       const uint4 vn = reinterpret_cast<const uint4*>(p.v_new + nrow)[c];
+      if constexpr (kNormRope)  // the new k row normalised and rotated first (all 64 lanes: wave-uniform branch)
+        kn = norm_rope_row(kn, reinterpret_cast<const uint4*>(p.k_norm_w)[c],
+                           rope_lane(p.cos_sin, min(max(p.positions[b], 0), p.max_pos - 1), c), p.eps, c);
       if (slot >= 0 && slot < p.num_slots) {
         if (r == 0) {
           const size_t dst = ((static_cast<size_t>(slot / kBlockSize) * p.Hkv + g) * kBlockSize + slot % kBlockSize) *

@@ -104,12 +104,31 @@ int fe_paged_gqa_decode_num_partitions(int B, int Hq, int Hkv, int D, int max_co
 
 namespace {
 
+// The norm/rotary inputs of fe_paged_gqa_decode_norm_rope_append.
+struct NormRopeIn {
+  const void* q_norm_w;
+  const void* k_norm_w;
+  const float* cos_sin;
+  int max_pos;
+  const int32_t* positions;
+  float eps;
+};
+
 int decode_call(const char* fn, void* out, float* lse, const void* q, const void* k_new, const void* v_new,
                 const int32_t* slot_mapping, bool fused, const void* k_cache, const void* v_cache,
                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens, int B, int Hq,
                 int Hkv, int D, int BS, int num_blocks, int max_context_len, float scale, int num_partitions,
-                void* workspace, size_t workspace_bytes, hipStream_t stream, bool use_scratch = false) {
+                void* workspace, size_t workspace_bytes, hipStream_t stream, bool use_scratch = false,
+                const NormRopeIn* nr = nullptr) {
   try {
+    if (nr) {
+      if (nr->max_pos <= 0) return fail(FE_ERR_INVALID_ARG, fn, "max_pos must be positive");
+      if (!isfinite(nr->eps) || nr->eps < 0.f) return fail(FE_ERR_INVALID_ARG, fn, "eps must be finite and >= 0");
+      if (B > 0 && (!nr->q_norm_w || !nr->k_norm_w || !nr->cos_sin || !nr->positions))
+        return fail(FE_ERR_NULL, fn, "q_norm_w, k_norm_w, cos_sin, positions must not be NULL");
+      if (!aligned16(nr->q_norm_w) || !aligned16(nr->k_norm_w) || !aligned16(nr->cos_sin))
+        return fail(FE_ERR_INVALID_ARG, fn, "the norm weights and cos_sin must be 16-byte aligned");
+    }
     if (B < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_partitions < 0)
       return fail(FE_ERR_INVALID_ARG, fn,
                   "B, max_context_len, num_partitions must be >= 0; num_blocks, max_blocks_per_seq positive");
@@ -153,6 +172,14 @@ int decode_call(const char* fn, void* out, float* lse, const void* q, const void
       a.v_new = v_new;
       a.new_slots = slot_mapping;
     }
+    if (nr) {
+      a.q_norm_w = nr->q_norm_w;
+      a.k_norm_w = nr->k_norm_w;
+      a.cos_sin = nr->cos_sin;
+      a.positions = nr->positions;
+      a.max_pos = nr->max_pos;
+      a.eps = nr->eps;
+    }
     const hipError_t e = fe::launch_decode(a, stream);
     return e == hipSuccess ? FE_OK : hip_fail(e, fn);
   } catch (...) {
@@ -189,6 +216,20 @@ int fe_paged_gqa_decode_append(void* out, float* lse, const void* q, const void*
   return decode_call("fe_paged_gqa_decode_append", out, lse, q, k_new, v_new, slot_mapping, true, k_cache, v_cache,
                      block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, num_blocks, max_context_len,
                      scale, num_partitions, workspace, workspace_bytes, stream);
+}
+
+int fe_paged_gqa_decode_norm_rope_append(void* out, float* lse, const void* q, const void* k_new, const void* v_new,
+                                         const void* q_norm_w, const void* k_norm_w, const float* cos_sin,
+                                         int max_pos, const int32_t* positions, const int32_t* slot_mapping,
+                                         void* k_cache, void* v_cache, const int32_t* block_tables,
+                                         int max_blocks_per_seq, const int32_t* context_lens, int B, int Hq, int Hkv,
+                                         int D, int BS, int num_blocks, int max_context_len, float scale, float eps,
+                                         int num_partitions, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  const NormRopeIn nr{q_norm_w, k_norm_w, cos_sin, max_pos, positions, eps};
+  return decode_call("fe_paged_gqa_decode_norm_rope_append", out, lse, q, k_new, v_new, slot_mapping, true, k_cache,
+                     v_cache, block_tables, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, num_blocks,
+                     max_context_len, scale, num_partitions, workspace, workspace_bytes, stream, false, &nr);
 }
 
 namespace {

@@ -53,6 +53,14 @@ struct DecodeArgs {
   const void* k_new = nullptr;
   const void* v_new = nullptr;
   const int32_t* new_slots = nullptr;
+  // fused norm/rotary of q and the new k (fe_paged_gqa_decode_norm_rope_append):
+  // nullptr q_norm_w means none
+  const void* q_norm_w = nullptr;
+  const void* k_norm_w = nullptr;
+  const float* cos_sin = nullptr;
+  const int32_t* positions = nullptr;
+  int max_pos = 0;
+  float eps = 0.f;
 };
 
 struct PrefillArgs {

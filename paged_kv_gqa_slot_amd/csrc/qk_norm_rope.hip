@@ -5,12 +5,10 @@
 // RMSNorm kernel and the paged KV cache).  Doing it in one pass keeps the
 // normed and rotated k from making a round trip through HBM before append.
 //
-// For each head row x (D = 128) of q and k:
-//   y = x * w / sqrt(mean(x^2) + eps)                    (per-head RMSNorm)
-//   rotate-half embedding, d < 64, table row p = positions[t]:
-//     y'[d] = y[d] c_d - y[d + 64] s_d,  y'[d + 64] = y[d + 64] c_d + y[d] s_d
-// in fp32, rounded once to bf16.  q rows go to q_out; k rows and the
-// unchanged v rows go to their cache slot.
+// Each head row x (D = 128) of q and k is normalised per head and rotated
+// (rotate-half embedding at table row positions[t]) as norm_rope_row.h
+// defines, in fp32, rounded once to bf16.  q rows go to q_out; k rows and
+// the unchanged v rows go to their cache slot.
 //
 // 16 lanes per 256-byte row, 16 bytes each: lane c holds dims 8c .. 8c + 7.
 // The sum of squares is a DPP reduction over the 16 lanes; the rotation
@@ -19,6 +17,7 @@
 
 #include "fe_device.h"
 #include "fe_kernels.h"
+#include "norm_rope_row.h"
 
 namespace fe {
 namespace {
@@ -56,15 +55,6 @@ struct NormRopeParams {
   float eps;
 };
 
-// Sum over the 16 lanes of a DPP row; every lane gets it.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp<kDppQuadXor1>(x);
-  x += dpp<kDppQuadXor2>(x);
-  x += dpp<kDppRowHalfMirror>(x);
-  x += dpp<kDppRowMirror>(x);
-  return x;
-}
-
 // One head row as this lane sees it: which token / kind / head, its slot, and
 // this lane's 16 bytes of the row.
 struct Row {
@@ -74,7 +64,7 @@ struct Row {
   int64_t slot;
   uint4 xw;
   uint4 ww;               // this lane's 8 norm weights
-  float4 c0, c1, s0, s1;  // this lane's cosines and sines
+  RopeLane cs;            // this lane's cosines and sines
 };
 
 // Each 16-lane group handles kRows rows, kRowGroups rows apart (a workgroup
@@ -134,12 +124,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeParams p
 #pragma unroll
   for (int k = 0; k < kRows; ++k) {
     Row& w = row[k];
-    const int d0 = 8 * (c & 7);  // angle index of this lane's first dim
-    const float4* cs = reinterpret_cast<const float4*>(p.cos_sin + static_cast<size_t>(w.pos) * kHeadDim + d0);
-    w.c0 = cs[0];
-    w.c1 = cs[1];
-    w.s0 = cs[16];  // the sines sit 64 floats further
-    w.s1 = cs[17];
+    w.cs = rope_lane(p.cos_sin, w.pos, c);
   }
 
 #pragma unroll
@@ -155,39 +140,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(NormRopeParams p
       continue;
     }
 
-    float x[8];
-    x[0] = bf16_lo(w.xw.x); x[1] = bf16_hi(w.xw.x);
-    x[2] = bf16_lo(w.xw.y); x[3] = bf16_hi(w.xw.y);
-    x[4] = bf16_lo(w.xw.z); x[5] = bf16_hi(w.xw.z);
-    x[6] = bf16_lo(w.xw.w); x[7] = bf16_hi(w.xw.w);
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ss = fmaf(x[j], x[j], ss);
-    ss = row_sum16(ss);
-    const float inv_rms = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + p.eps);
-
-    const uint4 ww = w.ww;
-    float y[8];
-    y[0] = x[0] * inv_rms * bf16_lo(ww.x); y[1] = x[1] * inv_rms * bf16_hi(ww.x);
-    y[2] = x[2] * inv_rms * bf16_lo(ww.y); y[3] = x[3] * inv_rms * bf16_hi(ww.y);
-    y[4] = x[4] * inv_rms * bf16_lo(ww.z); y[5] = x[5] * inv_rms * bf16_hi(ww.z);
-    y[6] = x[6] * inv_rms * bf16_lo(ww.w); y[7] = x[7] * inv_rms * bf16_hi(ww.w);
-
-    // the partner dims (d + 64 for lanes 0-7, d - 64 for lanes 8-15)
-    float z[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) z[j] = dpp<kDppRowRor8>(y[j]);
-
-    const float4 c0 = w.c0, c1 = w.c1, s0 = w.s0, s1 = w.s1;
-    const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    // first half: y c - z s; second half: y c + z s
-    const float sgn = c < 8 ? -1.0f : 1.0f;
-    float o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = fmaf(sgn * z[j], sv[j], y[j] * cv[j]);
-    const uint4 ow = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                                pack_bf16x2(o[6], o[7]));
+    const uint4 ow = norm_rope_row(w.xw, w.ww, w.cs, p.eps, c);
     if (!w.live) continue;
     if (w.kind == 0)
       store_nt(reinterpret_cast<uint4*>(p.q_out + (static_cast<size_t>(w.t) * p.Hq + w.head) * kHeadDim) + c, ow);

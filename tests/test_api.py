@@ -120,6 +120,38 @@ def test_decode_append_argument_errors(lib):
     assert dec_append(lib, B=0) == OK
 
 
+def dec_norm_rope(lib, **kw):
+    a = dict(out=P, lse=None, q=P, kn=P, vn=P, qw=P, kw=P, cs=P, mp=4096, pos=P, sm=P, k=P, v=P, bt=P, mb=8, cl=P,
+             B=2, Hq=32, Hkv=8, D=128, BS=16, NB=64, mcl=128, scale=0.088, eps=1e-6, parts=1, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return lib.fe_paged_gqa_decode_norm_rope_append(
+        a["out"], a["lse"], a["q"], a["kn"], a["vn"], a["qw"], a["kw"], a["cs"], a["mp"], a["pos"], a["sm"], a["k"],
+        a["v"], a["bt"], a["mb"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["BS"], a["NB"], a["mcl"], a["scale"],
+        a["eps"], a["parts"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_norm_rope_append_argument_errors(lib):
+    # everything the fused append + decode call checks ...
+    assert dec_norm_rope(lib, q=None) == NULL
+    assert dec_norm_rope(lib, sm=None) == NULL
+    assert dec_norm_rope(lib, Hq=30) == INVALID
+    assert dec_norm_rope(lib, D=64) == UNSUPPORTED
+    assert dec_norm_rope(lib, kn=P + 4) == INVALID
+    need = lib.fe_paged_gqa_decode_workspace_size(2, 32, 8, 128, 4096, 8)
+    assert dec_norm_rope(lib, mcl=4096, mb=256, parts=8, ws=P, wsb=need - 1) == WORKSPACE
+    # ... and the norm/rotary inputs
+    for name in ("qw", "kw", "cs", "pos"):
+        assert dec_norm_rope(lib, **{name: None}) == NULL
+        assert "positions" in fe.fe_last_error()
+    assert dec_norm_rope(lib, mp=0) == INVALID and "max_pos" in fe.fe_last_error()
+    assert dec_norm_rope(lib, eps=-1e-6) == INVALID
+    assert dec_norm_rope(lib, eps=float("nan")) == INVALID
+    assert dec_norm_rope(lib, cs=P + 4) == INVALID
+    assert dec_norm_rope(lib, qw=P + 2) == INVALID and "16-byte" in fe.fe_last_error()
+    assert dec_norm_rope(lib, B=0, qw=None, kw=None, cs=None, pos=None) == OK
+
+
 def test_workspace_and_partition_queries(lib):
     ws = lib.fe_paged_gqa_decode_workspace_size
     npart = lib.fe_paged_gqa_decode_num_partitions

@@ -128,6 +128,29 @@ def test_graph_decode_append(dev):
     replay_matches(step, [out, lse], dev, updated=[kc, vc])
 
 
+def test_graph_decode_norm_rope_append(dev):
+    """The one-launch attention step (norm/rotary of q and the new k, the
+    append, split-K decode) as a replayed graph."""
+    lens = [700, 1500, 64, 999, 16, 1]
+    w = inputs.custom("decode", 6, 32, 8, lens, 82, append=1)
+    c = inputs.norm_rope_case(w, 82)  # every sequence has one new token
+    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+    qw, kw, cs = c.q_norm_w.to(dev), c.k_norm_w.to(dev), c.cos_sin.to(dev)
+    pos, slots = c.positions.to(dev), c.slot_mapping.to(dev)
+    kc, vc = c.k_cache.to(dev), c.v_cache.to(dev)
+    bt, cl = w.block_tables.to(dev), w.context_lens.to(dev)
+    out = torch.empty(6, 32, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(6, 32, dtype=torch.float32, device=dev)
+    ws = torch.empty(fe.fe_paged_gqa_decode_workspace_size(6, 32, 8, 128, w.max_context_len, 4), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        fe.fe_paged_gqa_decode_norm_rope_append(out, lse, q, k, v, qw, kw, cs, pos, slots, kc, vc, bt, cl,
+                                                w.max_context_len, w.scale, c.eps, num_partitions=4, workspace=ws)
+
+    replay_matches(step, [out, lse], dev, updated=[kc, vc])
+
+
 def test_graph_sampler(dev):
     """The sampler step (two passes through a caller-owned workspace) as a
     replayed graph, the way the vocabulary benchmark launches it."""
