@@ -74,7 +74,7 @@ typedef enum {
   FE_OK = 0,
   FE_ERR_NULL = -1,         /* a required pointer is NULL */
   FE_ERR_INVALID_ARG = -2,  /* negative/zero size, Hq % Hkv != 0, non-finite scale, ... */
-  FE_ERR_UNSUPPORTED = -3,  /* a valid shape this build has no kernel for (D != 128, BS != 16, G > 8) */
+  FE_ERR_UNSUPPORTED = -3,  /* a valid shape the library has no kernel for (D != 128, BS != 16, G > 8) */
   FE_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than the size query returns */
   FE_ERR_HIP = -5,          /* the HIP runtime reported an error at launch */
   FE_ERR_INTERNAL = -6,
