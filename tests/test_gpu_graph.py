@@ -151,10 +151,12 @@ def test_graph_decode_norm_rope_append(dev):
     replay_matches(step, [out, lse], dev, updated=[kc, vc])
 
 
-def test_graph_sampler(dev):
-    """The sampler step (two passes through a caller-owned workspace) as a
-    replayed graph, the way the vocabulary benchmark launches it."""
-    c = inputs.sampler_case(64, inputs.QWEN3_VOCAB, seed=11)
+@pytest.mark.parametrize("B", [64, 256])
+def test_graph_sampler(dev, B):
+    """The sampler step as a replayed graph, the way the vocabulary
+    benchmark launches it: two passes through a caller-owned workspace at 64
+    rows, one workgroup per row at 256."""
+    c = inputs.sampler_case(B, inputs.QWEN3_VOCAB, seed=11)
     x, it = c.logits.to(dev), c.inv_temperature.to(dev)
     B, V = c.logits.shape
     probs = torch.empty(B, V, dtype=torch.float32, device=dev)
