@@ -97,7 +97,7 @@ def test_mixed_workspace_reuse(dev):
         assert int(ws[: 3 * 8 * 4].view(torch.int32).abs().sum()) == 0, "arrival counters not reset"
 
 
-@pytest.mark.parametrize("seed", [7])
+@pytest.mark.parametrize("seed", [7, 8, 9])
 def test_mixed_qwen3_4b_step(dev, seed):
     """The full mixed step (60 decode rows of 1024..8192 tokens and 4 chunks of
     256 after 4096 cached tokens) on every row."""
