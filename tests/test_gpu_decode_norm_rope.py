@@ -8,10 +8,17 @@ a copy of the pools; those k rows, read back from their slots, and q_out go
 into fe_paged_gqa_decode_append on a fresh copy.  The fused call must give
 the same out, lse and pools, bit for bit: it runs the same arithmetic with
 the same bf16 roundings.
-(2) Against the fp64 oracle (its norm/rotary step, then its decode) within
-the attention gate (max-abs 1e-2, row-relative 1e-2, LSE 1e-3), and the V
-pool bit for bit.  The K rows' own gate against the oracle is
-fe_qk_norm_rope_append's (its tests), to which (1) ties them.
+(2) Against the fp64 oracle (its norm/rotary step, then its decode), with
+the V pool bit for bit.  The q rows and the appended k rows are held to the
+norm/rotary gate (each within one bf16 step of the oracle's, few differing).
+The output and LSE are held to the attention gate (max-abs 1e-2,
+row-relative 1e-2, LSE 1e-3), widened row by row by the exact effect of
+those rows' differences: a q element that rounds to the other neighbouring
+bf16 value shifts every score of its row, and where the softmax is peaked
+one such flip alone moves the LSE by several 1e-4 (on the 64-sequence step
+below, 8 of 262144 q elements differ and one of them moves a row's LSE by
+5.6e-4; an fp32 emulation of the rows on the CPU gives the same figure).
+Rows whose q and keys equal the oracle's get no allowance.
 """
 import numpy as np
 import pytest
@@ -20,7 +27,7 @@ import torch
 import oracle
 import paged_kv_gqa_slot_amd as fe
 from paged_kv_gqa_slot_amd import inputs
-from gpu_util import assert_attention, u16
+from gpu_util import assert_attention, assert_rope_close, norm_only_rows, rope_term, rounding_allowance, u16
 
 pytestmark = pytest.mark.gpu
 
@@ -90,11 +97,24 @@ def run(w, c, dev, P, label, oracle_check=True):
         label, "lse differs from the composed step")
 
     if oracle_check:
-        rq, _, rkc, rvc = oracle.qk_norm_rope_append(c.q, c.k, c.v, c.q_norm_w, c.k_norm_w, c.cos_sin, c.positions,
-                                                     c.slot_mapping, c.k_cache, c.v_cache, c.eps)
-        assert np.array_equal(u16(vc_c), rvc), (label, "V pool differs from the oracle's")
+        rq, rk, rkc, rvc = oracle.qk_norm_rope_append(c.q, c.k, c.v, c.q_norm_w, c.k_norm_w, c.cos_sin, c.positions,
+                                                      c.slot_mapping, c.k_cache, c.v_cache, c.eps)
+        assert np.array_equal(va, rvc), (label, "V pool differs from the oracle's")
+        gq = u16(q_out)
+        assert_rope_close(gq, rq, rope_term(norm_only_rows(c.q, c.q_norm_w, c.eps), c.cos_sin, c.positions),
+                          f"{label} q rows")
+        sm_h = c.slot_mapping.numpy().astype(np.int64)
+        ok = (sm_h >= 0) & (sm_h < nslots)
+        kt = rope_term(norm_only_rows(c.k, c.k_norm_w, c.eps), c.cos_sin, c.positions)
+        assert_rope_close(ka[sm_h[ok] // 16, :, sm_h[ok] % 16, :], rk[ok], kt[ok], f"{label} k rows")
+        written = np.zeros(ka.shape[:1] + ka.shape[2:3], bool)
+        written[sm_h[ok] // 16, sm_h[ok] % 16] = True
+        outside = np.broadcast_to(~written[:, None, :, None], ka.shape)
+        assert np.array_equal(ka[outside], rkc[outside]), (label, "K pool changed outside the written slots")
         ro, rl = oracle.decode(rq, rkc, rvc, w.block_tables, w.context_lens, w.scale)
-        assert_attention(out_c, lse_c, ro, rl, f"{label} P={P}")
+        allow = rounding_allowance(gq, rq, ka, rkc, rvc, w.block_tables.numpy(), w.context_lens.numpy(), w.scale,
+                                      ro)
+        assert_attention(out_c, lse_c, ro, rl, f"{label} P={P}", allowance=allow)
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8])

@@ -19,11 +19,9 @@ import torch
 import oracle
 import paged_kv_gqa_slot_amd as fe
 from paged_kv_gqa_slot_amd import inputs
-from gpu_util import u16
+from gpu_util import assert_rope_close, norm_only_rows, rope_term, u16
 
 pytestmark = pytest.mark.gpu
-
-MISMATCH_FRAC = 1e-2
 
 
 @pytest.fixture(scope="module")
@@ -31,42 +29,6 @@ def dev():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     return torch.device("cuda:0")
-
-
-def bf16_values(bits: np.ndarray) -> np.ndarray:
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def ulp_bf16(v: np.ndarray) -> np.ndarray:
-    """Spacing of bf16 numbers at |v| (2^-133 below the normal range)."""
-    a = np.abs(v)
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    return np.where(a >= 2.0 ** -126, 2.0 ** (e - 7), 2.0 ** -133)
-
-
-def rope_term(y_bits: np.ndarray, cos_sin: torch.Tensor, positions: torch.Tensor) -> np.ndarray:
-    """|y_d c| + |y_p s| per element of [T][H][D] rows (p = partner of d)."""
-    y = bf16_values(y_bits)
-    T, H, Dm = y.shape
-    half = Dm // 2
-    cs = cos_sin.numpy().astype(np.float64)
-    pos = np.clip(positions.numpy(), 0, cs.shape[0] - 1)
-    c = np.abs(np.concatenate([cs[pos, :half], cs[pos, :half]], axis=1))[:, None, :]
-    s = np.abs(np.concatenate([cs[pos, half:], cs[pos, half:]], axis=1))[:, None, :]
-    partner = np.concatenate([y[..., half:], y[..., :half]], axis=-1)
-    return np.abs(y) * c + np.abs(partner) * s
-
-
-def assert_rope_close(got: np.ndarray, want: np.ndarray, term: np.ndarray, label: str):
-    assert got.shape == want.shape == term.shape, label
-    g, w = bf16_values(got), bf16_values(want)
-    err = np.abs(g - w)
-    bound = ulp_bf16(w) + 2.0 ** -20 * term
-    frac = float((got != want).mean()) if got.size else 0.0
-    worst = float((err / bound).max()) if got.size else 0.0
-    print(f"[{label}] worst err/bound {worst:.3f}, differing {frac:.2e}", flush=True)
-    assert np.all(err <= bound), (label, "bound", worst)
-    assert frac <= MISMATCH_FRAC, (label, "fraction", frac)
 
 
 def run_case(c: inputs.NormRopeCase, dev, label, in_place=False):
@@ -79,11 +41,8 @@ def run_case(c: inputs.NormRopeCase, dev, label, in_place=False):
     rq, rk_rows, rkc, rvc = oracle.qk_norm_rope_append(c.q, c.k, c.v, c.q_norm_w, c.k_norm_w, c.cos_sin,
                                                        c.positions, c.slot_mapping, c.k_cache, c.v_cache, c.eps)
     # |y| of the bound: the oracle's norm-only rows (a table whose every row is cos 1, sin 0)
-    ident = torch.zeros(1, 128)
-    ident[0, :64] = 1.0
-    zero = torch.zeros(c.positions.shape, dtype=torch.int32)
-    yq = oracle.norm_rope(c.q, c.q_norm_w, ident, zero, c.eps)
-    yk = oracle.norm_rope(c.k, c.k_norm_w, ident, zero, c.eps)
+    yq = norm_only_rows(c.q, c.q_norm_w, c.eps)
+    yk = norm_only_rows(c.k, c.k_norm_w, c.eps)
     assert_rope_close(u16(q_out), rq, rope_term(yq, c.cos_sin, c.positions), f"{label} q")
     gk, gv = u16(kc), u16(vc)
     assert np.array_equal(gv, rvc), f"{label}: V pool differs"
