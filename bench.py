@@ -581,6 +581,9 @@ def main():
                          "decode_norm_rope: that step and decode in one launch (decode workloads); "
                          "sampler: fp32 softmax + argmax over the Qwen3 vocabulary for --sampler-batch rows")
     ap.add_argument("--sampler-batch", type=int, default=64)
+    ap.add_argument("--split-weights", action="store_true",
+                    help="prefill workloads: the softmax weights enter the PV product as a bf16 value and its bf16 "
+                         "remainder (fe_paged_gqa_prefill_chunk_ex, split_weights 1) instead of rounded to bf16")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run 3 plain device copies of this many MiB (rocprofv3 counter calibration)")
     args = ap.parse_args()
@@ -621,6 +624,9 @@ def main():
     lse = torch.empty(total_q, w.Hq, dtype=torch.float32, device=dev)
     is_decode = spec.kind == "decode"
     is_mixed = spec.kind == "mixed"
+    if args.split_weights and (is_decode or is_mixed):
+        print("bench.py: --split-weights applies to prefill workloads", file=sys.stderr)
+        sys.exit(2)
     nd = spec.num_decode if is_mixed else 0
     if is_decode:
         P = fe.fe_paged_gqa_decode_num_partitions(w.B, w.Hq, w.Hkv, 128, mcl, args.partitions)
@@ -642,6 +648,9 @@ def main():
         elif is_mixed:
             fe.fe_paged_gqa_mixed(out, lse, x["q"], qsl, x["kc"], x["vc"], bt, lens, nd, max_q, mcl, w.scale,
                                   num_partitions=args.partitions, workspace=ws)
+        elif args.split_weights:
+            fe.fe_paged_gqa_prefill_chunk_ex(out, lse, x["q"], qsl, x["kc"], x["vc"], bt, lens, max_q, mcl, w.scale,
+                                             0, 1)
         else:
             fe.fe_paged_gqa_prefill_chunk(out, lse, x["q"], qsl, x["kc"], x["vc"], bt, lens, max_q, mcl, w.scale)
 
@@ -823,8 +832,10 @@ def main():
         achieved = flops / (att_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
-                "traffic": measured_traffic(spec.name, "prefill", 0),
-                "kernel": "fe_paged_gqa_prefill_chunk (gqa_prefill_chunk_kernel)", "per_launch_flops": flops,
+                "traffic": None if args.split_weights else measured_traffic(spec.name, "prefill", 0),
+                "kernel": "fe_paged_gqa_prefill_chunk_ex, split weights (gqa_prefill_chunk_kernel)"
+                if args.split_weights else "fe_paged_gqa_prefill_chunk (gqa_prefill_chunk_kernel)",
+                "per_launch_flops": flops,
                 "avg_ms": round(att_avg_ms, 5), "per_call_avg_ms": round(att_call_avg_ms, 5),
                 "median_ms": round(att_med_ms, 5), **att_spread,
                 "cold_median_ms": round(cold_med_ms, 5)}
@@ -850,6 +861,7 @@ def main():
            "block_size": 16, "layers": nl, "kv_tokens": w.kv_tokens, "max_context_len": mcl,
            "append_tokens_per_step": int(slots.numel()) * nl, "num_partitions": P, "seed": w.seed,
            "launch": launch, "settle_ms": args.settle_ms, "append": append_mode, "eager_ms_per_step": round(eager_ms, 5),
+           "split_weights": bool(args.split_weights) if not (is_decode or is_mixed) else None,
            "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
            "separate_append_ms_per_step": round(separate_ms, 5) if do_append else None,
            "fused_eager_ms_per_step": None if fused_eager_ms is None else round(fused_eager_ms, 5),

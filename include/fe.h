@@ -275,9 +275,9 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
                                int max_context_len, float scale, hipStream_t stream);
 
 /*
- * fe_paged_gqa_prefill_chunk with the kernel's tile shape chosen by the
- * caller; every other argument, the result's definition and the errors are
- * the same.
+ * fe_paged_gqa_prefill_chunk with the kernel's tile shape and the precision
+ * of the softmax weights in the PV product chosen by the caller; every other
+ * argument, the result's definition and the errors are the same.
  *   key_groups     0 = automatic (what fe_paged_gqa_prefill_chunk does);
  *                  1 = each workgroup walks its keys with one group of waves
  *                  (two workgroups fit on a compute unit);
@@ -293,13 +293,24 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
  * per compute unit, 3 above that (1 when a chunk has a single query tile or
  * Hq/Hkv = 3), and 1 for Hq/Hkv > 4.  The shapes differ only in the order of fp32
  * additions, so results agree within rounding, not bit for bit.
+ *   split_weights  0 = each softmax weight enters the PV product rounded to
+ *                  bf16 (what fe_paged_gqa_prefill_chunk does: at most 2^-8
+ *                  relative per weight); 1 = as two bf16 parts, the rounded
+ *                  weight and its rounded remainder (at most 2^-16 relative),
+ *                  which doubles the PV product's MFMA work (30-40% more
+ *                  time).  On a row dominated by two or three keys with
+ *                  output values near 2-4, the error of 0 plus the output's
+ *                  own bf16 rounding can exceed 1e-2; with 1 the error is
+ *                  the output's rounding alone.  Other values:
+ *                  FE_ERR_INVALID_ARG.
  * Source: as fe_paged_gqa_prefill_chunk.
  */
 int fe_paged_gqa_prefill_chunk_ex(void* out, float* lse, const void* q, const int32_t* query_start_loc,
                                   const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                   int max_blocks_per_seq, const int32_t* context_lens, int B, int total_q,
                                   int max_q_len, int Hq, int Hkv, int D, int BS, int num_blocks,
-                                  int max_context_len, float scale, int key_groups, hipStream_t stream);
+                                  int max_context_len, float scale, int key_groups, int split_weights,
+                                  hipStream_t stream);
 
 /*
  * Bytes of device workspace fe_paged_gqa_mixed needs for these sizes

@@ -59,7 +59,7 @@ def load_library():
     lib.fe_paged_gqa_decode_norm_rope_append.restype = I
     lib.fe_paged_gqa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, P]
     lib.fe_paged_gqa_prefill_chunk.restype = I
-    lib.fe_paged_gqa_prefill_chunk_ex.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, I, P]
+    lib.fe_paged_gqa_prefill_chunk_ex.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, F, I, I, P]
     lib.fe_paged_gqa_prefill_chunk_ex.restype = I
     lib.fe_paged_gqa_mixed_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.fe_paged_gqa_mixed_workspace_size.restype = Z
@@ -377,10 +377,12 @@ def fe_paged_gqa_prefill_chunk(out, lse, q, query_start_loc, k_cache, v_cache, b
 
 def fe_paged_gqa_prefill_chunk_ex(out, lse, q, query_start_loc, k_cache, v_cache, block_tables, context_lens,
                                   max_q_len: int, max_context_len: int, scale: float, key_groups: int,
-                                  stream=None) -> None:
+                                  split_weights: int = 0, stream=None) -> None:
     """fe_paged_gqa_prefill_chunk with the tile shape chosen by the caller
     (key_groups 0 automatic, 1 or 2 wave groups over the keys, 3 two query
-    tiles over one K/V stream)."""
+    tiles over one K/V stream) and the precision of the softmax weights in
+    the PV product (split_weights 0: rounded to bf16; 1: a bf16 value and
+    its bf16 remainder)."""
     _shape(q, "q", None, None, None)
     total_q, Hq, D = q.shape
     NB, Hkv, BS, _ = _pools(k_cache, v_cache)
@@ -392,7 +394,8 @@ def fe_paged_gqa_prefill_chunk_ex(out, lse, q, query_start_loc, k_cache, v_cache
         _dev(query_start_loc, torch.int32, "query_start_loc", 1), _dev(k_cache, torch.bfloat16, "k_cache", 4),
         _dev(v_cache, torch.bfloat16, "v_cache", 4), _dev(block_tables, torch.int32, "block_tables", 2),
         block_tables.shape[1], _dev(context_lens, torch.int32, "context_lens", 1), B, total_q, int(max_q_len),
-        Hq, Hkv, D, BS, NB, int(max_context_len), float(scale), int(key_groups), _stream(stream))
+        Hq, Hkv, D, BS, NB, int(max_context_len), float(scale), int(key_groups), int(split_weights),
+        _stream(stream))
     _check(rc, "fe_paged_gqa_prefill_chunk_ex")
 
 

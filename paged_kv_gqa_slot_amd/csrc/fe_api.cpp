@@ -237,9 +237,11 @@ namespace {
 int prefill_chunk(const char* fn, void* out, float* lse, const void* q, const int32_t* query_start_loc,
                   const void* k_cache, const void* v_cache, const int32_t* block_tables, int max_blocks_per_seq,
                   const int32_t* context_lens, int B, int total_q, int max_q_len, int Hq, int Hkv, int D, int BS,
-                  int num_blocks, int max_context_len, float scale, int key_groups, hipStream_t stream) {
+                  int num_blocks, int max_context_len, float scale, int key_groups, int split_weights,
+                  hipStream_t stream) {
   try {
     if (key_groups < 0 || key_groups > 3) return fail(FE_ERR_INVALID_ARG, fn, "key_groups must be 0, 1, 2 or 3");
+    if (split_weights != 0 && split_weights != 1) return fail(FE_ERR_INVALID_ARG, fn, "split_weights must be 0 or 1");
     if (B < 0 || total_q < 0 || max_q_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
       return fail(FE_ERR_INVALID_ARG, fn,
                   "B, total_q, max_q_len, max_context_len must be >= 0; num_blocks, max_blocks_per_seq positive");
@@ -257,7 +259,8 @@ int prefill_chunk(const char* fn, void* out, float* lse, const void* q, const in
       return fail(FE_ERR_INVALID_ARG, fn, "out, q, k_cache, v_cache must be 16-byte aligned");
     if (!launch_fits((max_q_len / 32.0 + 1) * Hkv * B, 512)) return fail(FE_ERR_UNSUPPORTED, fn, kTooLarge);
     fe::PrefillArgs a{out, lse, q, query_start_loc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
-                      B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale, key_groups};
+                      B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len, scale, key_groups,
+                      split_weights != 0};
     const hipError_t e = fe::launch_prefill(a, stream);
     return e == hipSuccess ? FE_OK : hip_fail(e, fn);
   } catch (...) {
@@ -274,17 +277,17 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
                                hipStream_t stream) {
   return prefill_chunk("fe_paged_gqa_prefill_chunk", out, lse, q, query_start_loc, k_cache, v_cache, block_tables,
                        max_blocks_per_seq, context_lens, B, total_q, max_q_len, Hq, Hkv, D, BS, num_blocks,
-                       max_context_len, scale, 0, stream);
+                       max_context_len, scale, 0, 0, stream);
 }
 
 int fe_paged_gqa_prefill_chunk_ex(void* out, float* lse, const void* q, const int32_t* query_start_loc,
                                   const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                   int max_blocks_per_seq, const int32_t* context_lens, int B, int total_q,
                                   int max_q_len, int Hq, int Hkv, int D, int BS, int num_blocks, int max_context_len,
-                                  float scale, int key_groups, hipStream_t stream) {
+                                  float scale, int key_groups, int split_weights, hipStream_t stream) {
   return prefill_chunk("fe_paged_gqa_prefill_chunk_ex", out, lse, q, query_start_loc, k_cache, v_cache,
                        block_tables, max_blocks_per_seq, context_lens, B, total_q, max_q_len, Hq, Hkv, D, BS,
-                       num_blocks, max_context_len, scale, key_groups, stream);
+                       num_blocks, max_context_len, scale, key_groups, split_weights, stream);
 }
 
 size_t fe_paged_gqa_mixed_workspace_size(int num_decode, int Hq, int Hkv, int D, int max_context_len,

@@ -76,6 +76,7 @@ struct PrefillArgs {
   int B, total_q, max_q_len, Hq, Hkv, num_blocks, max_context_len;
   float scale;
   int key_groups = 0;  // prefill tile: 0 automatic, 1 or 2 key groups, 3 two query tiles over one K/V stream
+  bool split_p = false;  // softmax weights into the PV product as two bf16 parts (rounded value + remainder)
 };
 
 // Mixed decode/prefill launch plan.  The decode sequences are split into

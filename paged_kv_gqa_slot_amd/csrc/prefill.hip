@@ -18,7 +18,7 @@ constexpr int kCuCount = 256;
 // One kernel per (group size, key groups).  Both shapes use at most 256
 // VGPRs, two waves per SIMD: one workgroup of two key groups per CU, or two
 // single-group workgroups per CU (each takes half the LDS).
-template <int G, int KSel>
+template <int G, int KSel, bool kSplitP>
 __global__ __launch_bounds__((Shape<G, KSel>::kThreads)) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 gqa_prefill_chunk_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[Shape<G, KSel>::kLdsBytes];
@@ -39,14 +39,15 @@ gqa_prefill_chunk_kernel(PrefillParams p) {
     pair = blockIdx.x % pairs;
     qt = blockIdx.x / pairs;
   }
-  prefill_tile<G, KSel>(p, lds, qt, pair / p.Hkv, pair % p.Hkv);
+  prefill_tile<G, KSel, kSplitP>(p, lds, qt, pair / p.Hkv, pair % p.Hkv);
 }
 
 template <int G, int KSel>
-hipError_t launch_shape(PrefillParams prm, long grid, hipStream_t stream) {
+hipError_t launch_shape(PrefillParams prm, long grid, bool split_p, hipStream_t stream) {
   void* args[] = {&prm};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gqa_prefill_chunk_kernel<G, KSel>),
-                         dim3(static_cast<unsigned>(grid)), dim3(Shape<G, KSel>::kThreads), args, 0, stream);
+  const void* fn = split_p ? reinterpret_cast<const void*>(&gqa_prefill_chunk_kernel<G, KSel, true>)
+                           : reinterpret_cast<const void*>(&gqa_prefill_chunk_kernel<G, KSel, false>);
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(Shape<G, KSel>::kThreads), args, 0, stream);
 }
 
 // Key groups per workgroup.  Two groups (8 waves, one workgroup per CU) pair
@@ -71,11 +72,11 @@ hipError_t launch_g(const PrefillArgs& a, const PrefillParams& prm, hipStream_t 
     constexpr bool kPairs = Shape<G>::W == 4;  // (G = 3 runs groups of 3 waves)
     const int ks =
         a.key_groups != 0 ? a.key_groups : (grid > kCuCount ? (kPairs && copy.qtiles > 1 ? 3 : 1) : 2);
-    if (ks == 1) return launch_shape<G, 1>(copy, grid, stream);
+    if (ks == 1) return launch_shape<G, 1>(copy, grid, a.split_p, stream);
     if constexpr (kPairs) {
       if (ks == 3) {
         const long pairs_grid = static_cast<long>((copy.qtiles + 1) / 2) * prm.Hkv * prm.B;
-        return launch_shape<G, 3>(copy, pairs_grid, stream);
+        return launch_shape<G, 3>(copy, pairs_grid, a.split_p, stream);
       }
     } else {
       if (ks == 3) return hipErrorInvalidValue;
@@ -83,7 +84,7 @@ hipError_t launch_g(const PrefillArgs& a, const PrefillParams& prm, hipStream_t 
   } else {
     if (a.key_groups >= 2) return hipErrorInvalidValue;
   }
-  return launch_shape<G, 0>(copy, grid, stream);
+  return launch_shape<G, 0>(copy, grid, a.split_p, stream);
 }
 
 }  // namespace

@@ -143,7 +143,10 @@ __device__ __forceinline__ void wait_vm() {
 
 // Query tile qt of sequence b against KV head g, run by the whole workgroup
 // (Shape<G, KSel>::kThreads threads); lds holds Shape<G, KSel>::kLdsBytes bytes.
-template <int G, int KSel = 0>
+// kSplitP: the softmax weights enter the PV product as two bf16 parts, the
+// rounded weight and the rounded remainder, so the product sees each weight
+// to within 2^-16 instead of 2^-8 (half again the MFMA work of a step).
+template <int G, int KSel = 0, bool kSplitP = false>
 __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned char* lds, int qt, int b, int g) {
   using S = Shape<G, KSel>;
   const int tid = threadIdx.x;
@@ -324,6 +327,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
 
   f32x16_t s[2];      // S^T of the current tile: keys 32 blk + 8 (i / 4) + 4 half + i % 4, query col
   bf16x8_t pb[2][2];  // P^T of the previous tile, k-step (blk, tau): S^T entries 8 tau .. 8 tau + 7
+  bf16x8_t pl[2][2];  // kSplitP: the remainders P^T - pb, rounded to bf16
 
   // S^T = K Q^T for the tile in LDS buffer `buf`
   auto qk = [&](auto bufc) __attribute__((always_inline)) {
@@ -347,6 +351,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   // O^T += V^T P^T for the tile in LDS buffer `buf`
   auto pv = [&](auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
+    bf16x8_t va[4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -362,8 +367,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
           // into half-word shuffles that drop the upper dword of each read
           const uint2 l2 = __builtin_bit_cast(uint2, lo);
           const uint2 h2 = __builtin_bit_cast(uint2, hi);
-          const bf16x8_t va = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
-          o_acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[blk][tau], o_acc[d], 0, 0, 0);
+          va[d] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+          o_acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d], pb[blk][tau], o_acc[d], 0, 0, 0);
+        }
+        if constexpr (kSplitP) {
+          // the remainders, each accumulator four MFMAs after its last use
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            o_acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[d], pl[blk][tau], o_acc[d], 0, 0, 0);
         }
       }
   };
@@ -403,6 +414,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
           w.z = pack_bf16x2(e[4], e[5]);
           w.w = pack_bf16x2(e[6], e[7]);
           pb[blk][tau] = as_bf16x8(w);
+          if constexpr (kSplitP) {
+            // e - bf16(e) is exact in fp32; its own rounding leaves at most 2^-16 of e
+            uint4 r;
+            r.x = pack_bf16x2(e[0] - bf16_lo(w.x), e[1] - bf16_hi(w.x));
+            r.y = pack_bf16x2(e[2] - bf16_lo(w.y), e[3] - bf16_hi(w.y));
+            r.z = pack_bf16x2(e[4] - bf16_lo(w.z), e[5] - bf16_hi(w.z));
+            r.w = pack_bf16x2(e[6] - bf16_lo(w.w), e[7] - bf16_hi(w.w));
+            pl[blk][tau] = as_bf16x8(r);
+          }
         }
       return (part[0] + part[1]) + (part[2] + part[3]);
     };
@@ -445,6 +465,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     qk(bufc);
     if constexpr (decltype(pvc)::value) {
       pv(Other{});
+      constexpr int kPvPer = kSplitP ? 2 : 1;  // MFMAs per pair of transposed V reads
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int j = 0; j < 12; ++j) {
@@ -453,7 +474,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kPvPer, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
 #pragma unroll

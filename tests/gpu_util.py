@@ -245,21 +245,22 @@ class DeviceWorkload:
         torch.cuda.synchronize()
         return out, lse
 
-    def prefill(self, max_q_len=None, key_groups=None):
+    def prefill(self, max_q_len=None, key_groups=None, split_weights=0):
         """fe_paged_gqa_prefill_chunk, or fe_paged_gqa_prefill_chunk_ex with
-        the given tile shape (key_groups 0, 1, 2 or 3)."""
+        the given tile shape (key_groups 0, 1, 2 or 3) and weight precision
+        (split_weights 0 or 1)."""
         w = self.w
         total_q = self.q.shape[0]
         out = torch.full((total_q, w.Hq, 128), float("nan"), dtype=torch.bfloat16, device=self.dev)
         lse = torch.full((total_q, w.Hq), float("nan"), dtype=torch.float32, device=self.dev)
         qsl = w.query_start_loc.tolist()
         mql = max(b - a for a, b in zip(qsl[:-1], qsl[1:])) if max_q_len is None else max_q_len
-        if key_groups is None:
+        if key_groups is None and not split_weights:
             fe.fe_paged_gqa_prefill_chunk(out, lse, self.q, self.qsl, self.kc, self.vc, self.bt, self.lens, mql,
                                           w.max_context_len, w.scale)
         else:
             fe.fe_paged_gqa_prefill_chunk_ex(out, lse, self.q, self.qsl, self.kc, self.vc, self.bt, self.lens, mql,
-                                             w.max_context_len, w.scale, key_groups)
+                                             w.max_context_len, w.scale, key_groups or 0, split_weights)
         torch.cuda.synchronize()
         return out, lse
 

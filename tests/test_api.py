@@ -201,11 +201,11 @@ def pre(lib, **kw):
 
 def pre_ex(lib, key_groups, **kw):
     a = dict(out=P, lse=None, q=P, qsl=P, k=P, v=P, bt=P, mb=8, cl=P, B=2, tq=16, mql=8, Hq=32, Hkv=8, D=128, BS=16,
-             NB=64, mcl=128, scale=0.088, stream=None)
+             NB=64, mcl=128, scale=0.088, split=0, stream=None)
     a.update(kw)
     return lib.fe_paged_gqa_prefill_chunk_ex(a["out"], a["lse"], a["q"], a["qsl"], a["k"], a["v"], a["bt"], a["mb"],
                                              a["cl"], a["B"], a["tq"], a["mql"], a["Hq"], a["Hkv"], a["D"], a["BS"],
-                                             a["NB"], a["mcl"], a["scale"], key_groups, a["stream"])
+                                             a["NB"], a["mcl"], a["scale"], key_groups, a["split"], a["stream"])
 
 
 def test_prefill_ex_key_groups_checks(lib):
@@ -225,6 +225,15 @@ def test_prefill_ex_key_groups_checks(lib):
     assert pre_ex(lib, 2, D=96) == UNSUPPORTED
     assert pre_ex(lib, 5, B=0) == INVALID
     assert "key_groups" in fe.fe_last_error()
+
+
+def test_prefill_ex_split_weights_checks(lib):
+    for kg in (0, 1, 3):
+        assert pre_ex(lib, kg, B=0, split=1) == OK
+    for bad in (-1, 2, 7):
+        assert pre_ex(lib, 0, B=0, split=bad) == INVALID
+        assert "split_weights" in fe.fe_last_error()
+    assert pre_ex(lib, 1, qsl=None, split=1) == NULL
 
 
 def test_prefill_argument_errors(lib):

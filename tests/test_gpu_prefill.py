@@ -6,6 +6,13 @@ context shorter than its chunk (rows with no visible key), the hand-derived
 golden example, prefill rows against the decode kernel, and the full 4 x
 (4096 + 256) and 64 x (1024 + 256) Qwen3-4B workloads on every row.  Gate: max-abs 1e-2,
 row-relative 1e-2, LSE 1e-3.
+
+The softmax weights enter the PV product rounded to bf16 (at most 2^-8
+relative each).  On a row that two or three keys dominate, with outputs near
+2-4, that error plus the output's own bf16 rounding (up to 7.8e-3 there) can
+pass max-abs 1e-2: the default form is held on such rows to the bound its
+arithmetic gives instead, and the split-weight form
+(fe_paged_gqa_prefill_chunk_ex, split_weights 1) to the gate.
 """
 import json
 import os
@@ -17,7 +24,7 @@ import torch
 import oracle
 import paged_kv_gqa_slot_amd as fe
 from paged_kv_gqa_slot_amd import inputs
-from gpu_util import DeviceWorkload, assert_attention
+from gpu_util import DeviceWorkload, assert_attention, attention_errors, beyond_output_rounding, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -29,13 +36,13 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run_prefill(w, dev, label, rows=None, lens_override=None, key_groups=None):
+def run_prefill(w, dev, label, rows=None, lens_override=None, key_groups=None, split_weights=0):
     dw = DeviceWorkload(w, dev)
     rk, rv = dw.append()
     lens = w.context_lens if lens_override is None else lens_override
     if lens_override is not None:
         dw.lens = lens_override.to(dev)
-    out, lse = dw.prefill(key_groups=key_groups)
+    out, lse = dw.prefill(key_groups=key_groups, split_weights=split_weights)
     ro, rl = oracle.prefill_chunk(dw.lay.q, w.query_start_loc, rk, rv, w.block_tables, lens, w.scale, rows=rows)
     if rows is not None:
         idx = torch.as_tensor(rows, dtype=torch.long, device=dev)
@@ -242,3 +249,73 @@ def test_prefill_qwen3_4b_b4_prefix4096_chunk256(dev, seed):
     """The chunked-prefill workload (4 x (4096 + 256)) on all 1024 rows."""
     w = inputs.make("qwen3_4b_b4_prefix4096_chunk256", seed=seed, poison="nan")
     run_prefill(w, dev, f"prefill 4b b4 seed {seed}")
+
+
+# Inputs of the small tile test (G = 8) whose rows of two or three keys with
+# |out| near 2.9 take the bf16-weight form past max-abs 1e-2 (found by a sweep
+# of 200 seeds).
+EDGE_SEEDS = [11000, 87000, 189000]
+
+
+def _edge_case(seed):
+    G = 8
+    lens = [64, 65, 128, 190, 257, 1000, 1088, 700]
+    chunks = [64, 1, 100, 190, 3, 300, 1, 129]
+    spec = inputs.Spec("prefill_ragged", "prefill", len(lens), 2 * G, 2, min(lens), max(lens), append=0, chunk=0)
+    return _ragged(spec, lens, chunks, seed + G, "nan")
+
+
+@pytest.mark.parametrize("seed", EDGE_SEEDS)
+def test_prefill_bf16_weights_within_their_bound(dev, seed):
+    """The default form on the edge inputs, against the bound its arithmetic
+    gives: each weight rounded to bf16 errs by at most 2^-8 of itself, so the
+    fp32 result errs by at most 2^-8 sum_j p_j |v_j| (the oracle's attention
+    over |V|) plus fp32 summation (1e-5 here), and the bf16 output adds half
+    a bf16 step of that value.  Row-relative error and LSE keep their gates."""
+    w = _edge_case(seed)
+    dw = DeviceWorkload(w, dev)
+    rk, rv = dw.append()
+    out, lse = dw.prefill()
+    lay = dw.lay
+    ro, rl = oracle.prefill_chunk(lay.q, w.query_start_loc, rk, rv, w.block_tables, w.context_lens, w.scale)
+    r_abs, _ = oracle.prefill_chunk(lay.q, w.query_start_loc, rk, rv & np.uint16(0x7fff), w.block_tables,
+                                    w.context_lens, w.scale)
+    o = out.float().cpu().numpy().astype(np.float64)
+    pre = 2.0 ** -8 * r_abs + 1e-5
+    bound = pre + 0.5 * ulp_bf16(np.abs(ro) + pre)
+    err = np.abs(o - ro)
+    max_abs, row_rel, lse_err = attention_errors(out, lse, ro, rl)
+    print(f"[edge seed {seed}] max_abs {max_abs:.3e} worst err/bound {float((err / bound).max()):.3f}", flush=True)
+    assert np.all(err <= bound), ("bound", float((err / bound).max()))
+    assert row_rel <= 1e-2 and lse_err <= 1e-3, (row_rel, lse_err)
+
+
+@pytest.mark.parametrize("seed", EDGE_SEEDS)
+def test_prefill_split_weights_edge_rows(dev, seed):
+    """The split-weight form on the same inputs: within the gate, and within
+    1e-4 of what rounding the exact result to bf16 costs (each weight to within
+    2^-16, |v| below 8 here)."""
+    w = _edge_case(seed)
+    dw = DeviceWorkload(w, dev)
+    rk, rv = dw.append()
+    out, lse = dw.prefill(split_weights=1)
+    ro, rl = oracle.prefill_chunk(dw.lay.q, w.query_start_loc, rk, rv, w.block_tables, w.context_lens, w.scale)
+    assert_attention(out, lse, ro, rl, f"split weights edge seed {seed}")
+    assert beyond_output_rounding(out, ro) <= 1e-4
+
+
+@pytest.mark.parametrize("G,kg", tile_cases([1, 3, 4, 8]))
+def test_prefill_split_weights_tile_counts(dev, G, kg):
+    """Every tile shape of the split-weight form on the tile-count inputs."""
+    lens = [64, 65, 128, 190, 257, 1000, 1088, 700]
+    chunks = [64, 1, 100, 190, 3, 300, 1, 129]
+    spec = inputs.Spec("prefill_ragged", "prefill", len(lens), 2 * G, 2, min(lens), max(lens), append=0, chunk=0)
+    w = _ragged(spec, lens, chunks, 400 + G, "nan")
+    dw, out, lse = run_prefill(w, dev, f"split weights G={G} key_groups={kg}", key_groups=kg if kg else 0,
+                               split_weights=1)
+
+
+def test_prefill_split_weights_qwen3_4b_b4(dev):
+    """The split-weight form on the 4 x (4096 + 256) workload, every row."""
+    w = inputs.make("qwen3_4b_b4_prefix4096_chunk256", seed=1, poison="nan")
+    run_prefill(w, dev, "split weights prefill 4b b4", split_weights=1)
