@@ -469,15 +469,19 @@ def bench_decode_norm_rope(args, w, fe, inputs, torch, dev):
     # the same rows reach the same slots every step, so the pools stay as they are
     ms, per, launch, eager_ms, graph_ms = time_calls(args, torch, fused)
     _, _, _, two_eager_ms, two_graph_ms = time_calls(args, torch, two_calls)
+    calibrate_copies(args, torch, dev)
     T = w.B
     nbytes = decode_bytes(w) + append_bytes(w) + T * (128 * 4 + 4) + 2 * 128 * 2  # + table rows, positions, weights
+    P = fe.fe_paged_gqa_decode_num_partitions(w.B, w.Hq, w.Hkv, 128, mcl, args.partitions)
     roof = {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(f"decode_norm_rope:{w.spec.name}", "decode", P),
             "kernel": "fe_paged_gqa_decode_norm_rope_append (gqa_decode_partition_kernel + gqa_decode_merge_kernel)",
             "per_launch_bytes": nbytes, "avg_ms": round(ms, 5), "per_call_avg_ms": round(sum(per) / len(per), 5),
             "median_ms": round(per[len(per) // 2], 5), **spread(per)}
     cfg = {"workload": f"decode_norm_rope:{w.spec.name}", "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
-           "head_dim": 128, "block_size": 16, "max_context_len": mcl, "seed": w.seed, "launch": launch,
+           "head_dim": 128, "block_size": 16, "max_context_len": mcl, "num_partitions": P, "seed": w.seed,
+           "launch": launch,
            "settle_ms": args.settle_ms, "eager_ms_per_step": round(eager_ms, 5),
            "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
            "two_calls_eager_ms_per_step": round(two_eager_ms, 5),
