@@ -458,7 +458,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
   // cyclically).  One basic block; the
   // scheduling groups keep four MFMA operands in flight from LDS so the read
   // latency hides behind the MFMAs (16 K reads of 16 bytes for S^T, then two
-  // 8-byte transposed V reads per PV MFMA).
+  // 8-byte transposed V reads per PV MFMA, or per pair of them with kSplitP).
   auto mphase = [&](auto bufc, auto pvc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     using Other = std::integral_constant<int, (buf + S::kBufs - 1) % S::kBufs>;
