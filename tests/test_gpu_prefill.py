@@ -319,3 +319,10 @@ def test_prefill_split_weights_qwen3_4b_b4(dev):
     """The split-weight form on the 4 x (4096 + 256) workload, every row."""
     w = inputs.make("qwen3_4b_b4_prefix4096_chunk256", seed=1, poison="nan")
     run_prefill(w, dev, "split weights prefill 4b b4", split_weights=1)
+
+
+def test_prefill_split_weights_qwen3_4b_b64(dev):
+    """The split-weight form on the 64 x (1024 + 256) step, where the
+    automatic shape takes two query tiles per workgroup; every row."""
+    w = inputs.make("qwen3_4b_b64_prefix1024_chunk256", poison="nan")
+    run_prefill(w, dev, "split weights prefill 4b b64 prefix 1024", split_weights=1)
