@@ -300,8 +300,8 @@ int fe_paged_gqa_prefill_chunk(void* out, float* lse, const void* q, const int32
  *                  which doubles the PV product's MFMA work (30-40% more
  *                  time).  On a row dominated by two or three keys with
  *                  output values near 2-4, the error of 0 plus the output's
- *                  own bf16 rounding can exceed 1e-2; with 1 the error is
- *                  the output's rounding alone.  Other values:
+ *                  own bf16 rounding can exceed 1e-2; with 1 what remains
+ *                  is essentially the output's own rounding.  Other values:
  *                  FE_ERR_INVALID_ARG.
  * Source: as fe_paged_gqa_prefill_chunk.
  */
