@@ -111,8 +111,8 @@ __global__ __launch_bounds__(kThreads) void sampler_partial_kernel(SamplerParams
 #pragma unroll
   for (int k = 0; k < kUnitsPerThread; ++k) {
     const int u = u0 + threadIdx.x + k * kThreads;
-    // plain (cached) loads: pass 2 reads the same logits again, on the same
-    // XCD (same grid mapping), and finds them in its L2
+    // plain loads: non-temporal ones were 1-2% slower; pass 2 fetches the
+    // logits past the L2 either way (it does not keep them across launches)
     w[k] = u < u1 ? *reinterpret_cast<const u32x4_t*>(&row[u]) : u32x4_t{0, 0, 0, 0};
   }
 #pragma unroll
