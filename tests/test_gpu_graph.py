@@ -3,8 +3,8 @@ step): every replay, with other GPU work run eagerly in between, must give
 exactly the results of the same calls launched eagerly (the kernels reduce in
 a fixed order, so the outputs are bit-identical).  Covers KV append + split-K
 decode (pass 1 + merge), the mixed launch (in-kernel merge through the
-workspace counters), append fused into decode, the fused norm/rotary/append step
-and the sampler."""
+workspace counters), append fused into decode, the fused norm/rotary/append step,
+append + prefill (both weight forms) and the sampler."""
 import pytest
 import torch
 
@@ -168,3 +168,21 @@ def test_graph_sampler(dev, B):
         fe.fe_sampler_softmax_argmax(probs, lse, am, x, it, workspace=ws)
 
     replay_matches(step, [probs, lse, am], dev)
+
+
+@pytest.mark.parametrize("split", [0, 1])
+def test_graph_prefill(dev, split):
+    """KV append of the chunks, then the prefill call (split_weights 0 and 1)."""
+    w = inputs.custom("prefill", 3, 32, 8, [300, 90, 1100], 806, append=70, chunk=70)
+    lay = w.layers[0]
+    kc, vc = lay.k_cache.to(dev), lay.v_cache.to(dev)
+    kn, vn, sm = lay.k_new.to(dev), lay.v_new.to(dev), w.slot_mapping.to(dev)
+    q, qsl, bt, cl = lay.q.to(dev), w.query_start_loc.to(dev), w.block_tables.to(dev), w.context_lens.to(dev)
+    out = torch.empty(q.shape[0], 32, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[0], 32, dtype=torch.float32, device=dev)
+
+    def step():
+        fe.fe_paged_kv_append(kn, vn, sm, kc, vc)
+        fe.fe_paged_gqa_prefill_chunk_ex(out, lse, q, qsl, kc, vc, bt, cl, 70, w.max_context_len, w.scale, 0, split)
+
+    replay_matches(step, [out, lse], dev, updated=[kc, vc])
